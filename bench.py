@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+Default workload: the Llama-3-8B-shaped decode step (64 sequences, context
+lengths uniform in [128, 4096], 32 query / 8 kv heads x 128, bf16, 16-token
+blocks in a shuffled pool at 90% fill).  One step = the cache write of the 64
+new tokens + the paged decode attention of the 64 sequences, on inputs already
+resident in HBM.
+
+Prints one JSON line.  `value` is the KV bytes the decode step reads per
+second (GB/s, whole job); the line also carries seq-tokens/s, the roofline of
+the decode call (HIP events around every timed call, on the stream the
+library launches on) and the CPU oracle timed on the host as a reported
+baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cold] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV HBM GB/s (% of peak) + seq-tokens/s, 8B-shaped batch"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+WORKLOADS = {
+    "llama3-8b-decode": 2,
+    "tiny-decode-f32": 1,
+    "mixed-step": 3,
+    "shared-prefix": 4,
+    "long-context": 5,
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama3-8b-decode", choices=sorted(WORKLOADS))
+    p.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = automatic)")
+    p.add_argument("--cold", action="store_true", help="overwrite 512 MB before every step (LLC-cold timing)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(how the path would shard across GPUs is described in the design notes)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_295_amd as pkv
+    import workloads
+    from workloads import accounting
+
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[args.workload]
+    w = workloads.make(cfg)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.int32:
+            return torch.from_numpy(a).to(dev)
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    kc, vc = to_dev(w.k_cache), to_dev(w.v_cache)
+    nk, nv, slots = to_dev(w.new_k), to_dev(w.new_v), to_dev(w.slot_mapping)
+    q, tables, lens = to_dev(w.q), to_dev(w.block_tables), to_dev(w.context_lens)
+    out = torch.empty_like(q)
+    has_chunks = w.num_chunks > 0
+    if has_chunks:
+        qc, cstart, ctables, clens = (to_dev(w.q_chunk), to_dev(w.chunk_start), to_dev(w.chunk_tables),
+                                      to_dev(w.chunk_context_lens))
+        oc = torch.empty_like(qc)
+    part = args.partition or pkv.decode_partition_tokens(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                                         w.max_context_len)
+    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                          w.max_context_len, part)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if args.cold else None
+    scale = float(w.scale)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        pkv.paged_kv_write(nk, nv, slots, kc, vc)
+        if ev:
+            ev[1].record()
+        if w.num_seqs:
+            pkv.paged_attn_decode(q, kc, vc, tables, lens, scale, out, max_context_len=w.max_context_len,
+                                  partition_tokens=part, workspace=ws)
+        if ev:
+            ev[2].record()
+        if has_chunks:
+            pkv.paged_attn_prefill_chunk(qc, cstart, kc, vc, ctables, clens, scale, oc)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if flush is not None:
+            flush.zero_()
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    write_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    pre_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms_events = write_ms + dec_ms + pre_ms
+    ms_per_step = (wall * 1e3 / K) if flush is None else float(step_ms_events.mean())
+
+    eb = w.elem_bytes
+    dec = accounting.decode_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
+                                  block_tables=w.block_tables, dedupe_shared=(cfg == 4))
+    kv_bytes = dec["kv"]
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    seq_tok_s = w.num_seqs / (ms_per_step * 1e-3)
+    dec_mean = float(dec_ms.mean())
+    achieved = dec["total"] / (dec_mean * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "paged_attn_decode (partition + merge kernels)", "bytes_per_launch": dec["total"],
+                "launch_ms_mean": round(dec_mean, 5), "launch_ms_median": round(float(np.median(dec_ms)), 5)}
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "seed": w.seed, "num_seqs": w.num_seqs,
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": 16, "num_blocks": w.num_blocks, "context_tokens": int(w.context_lens.sum()),
+                   "max_context_len": w.max_context_len, "partition_tokens": part,
+                   "kv_bytes_per_step": kv_bytes, "llc": "cold (512 MB overwrite per step)" if args.cold else "warm",
+                   "layers_per_step": 1},
+        "seq_tokens_per_s": round(seq_tok_s, 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "write_ms_mean": round(float(write_ms.mean()), 5),
+        "decode_ms_mean": round(dec_mean, 5),
+        "roofline": roofline,
+    }
+    if has_chunks:
+        flops = accounting.prefill_flops(w.chunk_start, w.chunk_context_lens, w.num_q_heads, w.head_dim)
+        pm = float(pre_ms.mean())
+        res["prefill"] = {"ms_mean": round(pm, 5), "flops": flops,
+                          "tflops": round(flops / (pm * 1e-3) / 1e12, 2),
+                          "mfma_frac_of_bf16_peak": round(flops / (pm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, cfg)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, seconds, cfg):
+    """The fp64 oracle (write + decode of the same step) timed on one host thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import accounting
+
+    # sample: whole sequences of the batch, in order, until ~`seconds` of CPU work
+    done_seqs, done_tokens, t_total, reps = 0, 0, 0.0, 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        rk, rv = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
+        t_total += time.perf_counter() - t0
+        while t_total < seconds:
+            for s in range(w.num_seqs):
+                t0 = time.perf_counter()
+                oracle.decode(w.q[s:s + 1], rk, rv, w.block_tables[s:s + 1], w.context_lens[s:s + 1], w.scale,
+                              w.dtype)
+                t_total += time.perf_counter() - t0
+                done_seqs += 1
+                done_tokens += int(w.context_lens[s])
+                if t_total >= seconds:
+                    break
+            reps += 1
+    row = w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
+    return {"value": round(done_tokens * row / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seq_tokens_per_s": round(done_seqs / t_total, 2),
+            "sample": f"fp64 numpy oracle, one thread: cache write of the step's {len(w.slot_mapping)} rows + decode "
+                      f"of {done_seqs} sequences taken in batch order ({done_tokens} context tokens), "
+                      f"{t_total:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

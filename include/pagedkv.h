@@ -1,0 +1,178 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The cache organisation follows the pages this library is built from:
+ *   - the ainews.alishangtian.com article on inference engines, section
+ *     "PagedAttention": the KV cache is cut into fixed-size blocks (usually 16
+ *     tokens), allocated on demand and chained per request by a block table;
+ *     requests with a common prefix reference the same physical blocks;
+ *   - "Part 47 | Inference basics: KV Cache, batching, sampling"
+ *     (chengxuchu.com): section 2.1 (softmax(Q K^T / sqrt(d)) V, the query of
+ *     position t reads keys 1..t), section 2.2 (decode appends the new K/V to
+ *     the cache, then its query reads the whole cache; production code writes
+ *     the new K/V into preallocated pages at a given position), section 2.3
+ *     (cache shape and GQA: fewer kv heads than query heads), section 5.2
+ *     (the GPU kernel finds each token's K/V through the block table);
+ *   - the caffein.top essay on modern LLM inference runtimes, sections on
+ *     chunked prefill (a long prompt is processed in chunks interleaved with
+ *     decode steps) and on paging (logically contiguous tokens live in
+ *     non-contiguous physical blocks).
+ *
+ * Layouts (all row-major, contiguous, device memory owned by the caller):
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][16][head_dim]
+ *                     slot s = physical_block * 16 + offset_in_block
+ *   block_tables      int32 [rows][max_blocks_per_seq]; entry j is the
+ *                     physical block of logical tokens 16j .. 16j+15
+ *   q (decode)        [num_seqs][num_q_heads][head_dim]
+ *   q_chunk           [num_chunks][chunk_len_max][num_q_heads][head_dim]
+ *   out               same shape and dtype as q / q_chunk
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ * Element type: float32 or bfloat16, the same for caches, k, v, q and out.
+ * Accumulation is float32; a bf16 output is rounded to nearest even.
+ *
+ * Every call is asynchronous on `hip_stream` (a hipStream_t; NULL means the
+ * default stream).  The library allocates nothing, keeps no pointer after
+ * return and holds no state.  Arguments are validated on the host only
+ * (nothing is read back from the device); on a non-zero return nothing was
+ * launched.  Device-resident values that break the contract below are not
+ * reported by a return code; the kernels never read or write outside the
+ * buffers described here because of them, and the affected outputs are set
+ * to NaN (or, for the write, the row is skipped) as each function states.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PKV_OK 0
+#define PKV_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PKV_ERR_DTYPE (-2)       /* dtype is neither PKV_DTYPE_F32 nor PKV_DTYPE_BF16 */
+#define PKV_ERR_SHAPE (-3)       /* a size is negative/zero where it must be positive, Hq % Hkv != 0,
+                                    max_context_len > 16 * max_blocks_per_seq, or index range overflow */
+#define PKV_ERR_UNSUPPORTED (-4) /* block_size != 16, or head_dim not 64 or 128 */
+#define PKV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than the query function requires */
+#define PKV_ERR_HIP (-6)         /* a kernel launch failed (hipGetLastError after launch) */
+
+#define PKV_DTYPE_F32 0
+#define PKV_DTYPE_BF16 1
+#define PKV_BLOCK_SIZE 16
+
+/* Description of one layer's paged cache (both K and V use it). */
+typedef struct pkv_cache_desc {
+  int32_t num_blocks;   /* physical blocks in the pool, >= 1 */
+  int32_t block_size;   /* tokens per block; must be 16 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t dtype;        /* PKV_DTYPE_F32 or PKV_DTYPE_BF16 */
+} pkv_cache_desc;
+
+/*
+ * paged_kv_write -- scatter new K/V rows into their cache slots.
+ * ("Part 47", section 2.2: the new token's K/V are written at a given
+ * position of preallocated pages before the query reads the cache.)
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   slot_mapping  int32 [num_tokens]; row i goes to block slot_mapping[i] / 16,
+ *                 offset slot_mapping[i] % 16, for every kv head
+ *   k_cache, v_cache   updated in place
+ *
+ * A raw copy of the bit patterns (bit-exact).  A negative slot skips its row
+ * (lets a caller pad); a slot >= 16 * num_blocks is also skipped.  Two rows with
+ * the same slot in one call leave either row there (unspecified which).
+ * num_tokens == 0 is a no-op that returns PKV_OK.
+ */
+int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int64_t num_tokens,
+                   void* k_cache, void* v_cache, const pkv_cache_desc* cache, void* hip_stream);
+
+/*
+ * Split-context decode: a sequence's context is cut into partitions of
+ * `partition_tokens` tokens (a multiple of 16); each partition's running max,
+ * sum of exponentials and unnormalised output are combined by a log-sum-exp
+ * merge, which equals the one-pass softmax in exact arithmetic.
+ *
+ * paged_attn_decode_partition_tokens returns the partition size used when
+ * paged_attn_decode is called with partition_tokens == 0 (a function of the
+ * batch shape only).  paged_attn_decode_workspace_bytes returns the workspace
+ * paged_attn_decode needs for these sizes (0 if every sequence fits one
+ * partition); partition_tokens == 0 means the automatic choice.
+ */
+int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t max_context_len);
+size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ * paged_attn_decode -- one continuous-batching decode step: for every sequence
+ * s and query head h,
+ *     out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
+ * over the first context_lens[s] tokens of sequence s, reached through
+ * block_tables[s].  ("Part 47", sections 2.1-2.2; the new token's K/V must
+ * already be in the cache, so its query sits at position context_lens[s]-1.)
+ *
+ *   q, out            [num_seqs][num_q_heads][head_dim]
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens      int32 [num_seqs] (device); context_lens[s] == 0 gives out = 0
+ *   max_context_len   host-side upper bound of context_lens (sizes the grid)
+ *   scale             softmax scale, usually 1/sqrt(head_dim)
+ *   partition_tokens  0 = automatic, else a positive multiple of 16
+ *   workspace         device scratch of at least
+ *                     paged_attn_decode_workspace_bytes(...) bytes (may be
+ *                     NULL when that is 0); contents need no initialisation
+ *
+ * Device-side contract: 0 <= context_lens[s] <= max_context_len and the first
+ * ceil(context_lens[s]/16) table entries lie in [0, num_blocks).  A sequence
+ * that breaks it gets NaN in every output row of the heads concerned.
+ * num_seqs == 0 is a no-op.
+ */
+int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                      const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                      float scale, void* out, int32_t partition_tokens, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
+
+/*
+ * paged_attn_prefill_chunk -- causal attention for chunks of prompts whose
+ * K/V (including the chunk's own rows) are already in the cache.
+ * (caffein.top essay, section on chunked prefill; "Part 47", section 2.1 for
+ * the causal rule.)
+ *
+ *   q_chunk, out      [num_chunks][chunk_len_max][num_q_heads][head_dim]
+ *   chunk_start       int32 [num_chunks] (device): position of the chunk's row 0
+ *   context_lens      int32 [num_chunks] (device): tokens in the cache for the
+ *                     chunk's sequence, through the chunk's last row
+ *   block_tables      int32 [num_chunks][max_blocks_per_seq]
+ *
+ * Chunk c has n_c = context_lens[c] - chunk_start[c] rows; row i (i < n_c)
+ * sits at position chunk_start[c] + i and attends to keys 0 .. chunk_start[c]+i.
+ * Rows i >= n_c of out are not written.  Device-side contract:
+ * 0 <= chunk_start[c] <= context_lens[c] <= 16 * max_blocks_per_seq,
+ * n_c <= chunk_len_max, and table entries in range; a chunk that breaks it gets
+ * NaN in its valid rows (rows up to chunk_len_max for n_c too large).
+ * bf16 runs on the matrix cores (MFMA); float32 runs on the vector ALUs.
+ * num_chunks == 0 is a no-op.
+ */
+int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t chunk_len_max,
+                             int32_t num_q_heads, const int32_t* chunk_start, const void* k_cache,
+                             const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
+                             void* out, void* hip_stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int32_t pkv_abi_version(void);
+#define PKV_ABI_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

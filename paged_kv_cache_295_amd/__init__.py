@@ -1,0 +1,202 @@
+"""Attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of libpagedkv.so (include/pagedkv.h).  It only marshals
+arguments -- tensor pointers, sizes read from tensor shapes, the current HIP
+stream -- and raises PagedKVError on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback, so a
+missing library is an error.
+
+PyTorch provides device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "PagedKVError", "load_library", "paged_kv_write", "paged_attn_decode", "paged_attn_prefill_chunk",
+    "decode_workspace_bytes", "decode_partition_tokens", "library_path", "BLOCK_SIZE",
+]
+
+BLOCK_SIZE = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpagedkv.so"
+_lib = None
+
+PKV_DTYPE_F32 = 0
+PKV_DTYPE_BF16 = 1
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _lib.pkv_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.environ.get("PAGEDKV_LIB", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load libpagedkv.so (built in-tree by paged_kv_cache_295_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_295_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    cdp = ctypes.POINTER(CacheDesc)
+    lib.paged_kv_write.argtypes = [vp, vp, vp, i64, vp, vp, cdp, vp]
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_attn_decode_partition_tokens.argtypes = [i32, i32, i32, i32]
+    lib.paged_attn_decode_partition_tokens.restype = i32
+    lib.paged_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attn_decode_workspace_bytes.restype = sz
+    lib.paged_attn_decode.argtypes = [vp, i32, i32, vp, vp, cdp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp]
+    lib.paged_attn_decode.restype = ctypes.c_int
+    lib.paged_attn_prefill_chunk.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp]
+    lib.paged_attn_prefill_chunk.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_abi_version.argtypes = []
+    lib.pkv_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PKV_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t) -> int:
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _i32(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _ptr(t)
+
+
+def _same_dtype(*ts):
+    d = ts[0].dtype
+    for t in ts[1:]:
+        if t.dtype != d:
+            raise TypeError("q/out/k/v/caches must share one dtype")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _cache_desc(k_cache) -> CacheDesc:
+    if k_cache.dim() != 4 or k_cache.shape[2] != BLOCK_SIZE:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, 16, head_dim]")
+    nb, hkv, _, d = k_cache.shape
+    return CacheDesc(nb, BLOCK_SIZE, hkv, d, _dtype_code(k_cache))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise PagedKVError(status, what)
+
+
+def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """Store row i of k/v ([T, Hkv, D]) at cache slot slot_mapping[i] (int32 [T])."""
+    lib = load_library()
+    _same_dtype(k, v, k_cache, v_cache)
+    desc = _cache_desc(k_cache)
+    if k.shape[1:] != (desc.num_kv_heads, desc.head_dim) or v.shape != k.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("k, v must be [T, num_kv_heads, head_dim] matching the caches")
+    if slot_mapping.shape != (k.shape[0],):
+        raise ValueError("slot_mapping must be [T]")
+    st = lib.paged_kv_write(_ptr(k), _ptr(v), _i32(slot_mapping, "slot_mapping"), k.shape[0], _ptr(k_cache),
+                            _ptr(v_cache), ctypes.byref(desc), _stream(stream))
+    _check(st, "paged_kv_write")
+
+
+def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, max_context_len) -> int:
+    return int(load_library().paged_attn_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads,
+                                                                 max_context_len))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                           partition_tokens=0) -> int:
+    return int(load_library().paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                                max_context_len, partition_tokens))
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,
+                      partition_tokens=0, workspace=None, stream=None):
+    """out[s, h] = softmax(scale q[s, h] K_s^T) V_s over the first context_lens[s] cached tokens.
+
+    max_context_len: host-side bound on context_lens (defaults to the block
+    table's capacity, 16 * block_tables.shape[1]).  workspace: optional uint8
+    device tensor; allocated here when needed and not given.
+    """
+    lib = load_library()
+    _same_dtype(q, out, k_cache, v_cache)
+    desc = _cache_desc(k_cache)
+    B, hq, d = q.shape
+    if out.shape != q.shape or d != desc.head_dim:
+        raise ValueError("q/out must be [B, Hq, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables [B, max_blocks], context_lens [B]")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * BLOCK_SIZE
+    need = decode_workspace_bytes(B, hq, desc.num_kv_heads, d, max_context_len, partition_tokens)
+    if need and workspace is None:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.paged_attn_decode(_ptr(q), B, hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                               _i32(block_tables, "block_tables"), max_blocks, _i32(context_lens, "context_lens"),
+                               int(max_context_len), float(scale), _ptr(out), int(partition_tokens), ws_ptr,
+                               ws_bytes, _stream(stream))
+    _check(st, "paged_attn_decode")
+    return out
+
+
+def paged_attn_prefill_chunk(q_chunk, chunk_start, k_cache, v_cache, block_tables, context_lens, scale, out,
+                             stream=None):
+    """Causal attention of each chunk's rows (q_chunk [Nc, Cmax, Hq, D]) over its cached context."""
+    lib = load_library()
+    _same_dtype(q_chunk, out, k_cache, v_cache)
+    desc = _cache_desc(k_cache)
+    nc, cmax, hq, d = q_chunk.shape
+    if out.shape != q_chunk.shape or d != desc.head_dim:
+        raise ValueError("q_chunk/out must be [Nc, Cmax, Hq, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != nc or chunk_start.shape != (nc,) \
+            or context_lens.shape != (nc,):
+        raise ValueError("block_tables [Nc, max_blocks], chunk_start [Nc], context_lens [Nc]")
+    st = lib.paged_attn_prefill_chunk(_ptr(q_chunk), nc, cmax, hq, _i32(chunk_start, "chunk_start"),
+                                      _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                                      _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                      _i32(context_lens, "context_lens"), float(scale), _ptr(out),
+                                      _stream(stream))
+    _check(st, "paged_attn_prefill_chunk")
+    return out

@@ -1,0 +1,194 @@
+// C ABI of libpagedkv.so: host-side validation, partition sizing and launches.
+// Nothing here reads device memory or synchronises; every launch goes to the
+// caller's stream.  See include/pagedkv.h for the contract of each call.
+#include <math.h>
+
+#include "pagedkv.h"
+#include "pkv_internal.hpp"
+
+using namespace pkv;
+
+namespace {
+
+int check_cache(const pkv_cache_desc* c) {
+  if (c == nullptr) return PKV_ERR_NULL;
+  if (c->dtype != PKV_DTYPE_F32 && c->dtype != PKV_DTYPE_BF16) return PKV_ERR_DTYPE;
+  if (c->block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PKV_ERR_SHAPE;
+  // slots and per-block offsets are int32 on the device
+  if ((int64_t)c->num_blocks * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+constexpr int32_t kMinPartition = 256;
+constexpr int32_t kMaxPartition = 16384;
+// Work items the automatic partition size aims for: about eight waves per
+// compute unit on a 256-CU MI355X.
+constexpr int64_t kTargetItems = 2048;
+
+int32_t auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads <= 0) return kMinPartition;
+  const int64_t waves_per_part =
+      (int64_t)num_seqs * num_kv_heads * ((num_q_heads / num_kv_heads) / heads_per_wave(num_q_heads / num_kv_heads));
+  int32_t best = kMinPartition;
+  for (int32_t p = kMinPartition; p <= kMaxPartition; p *= 2) {
+    // contexts are assumed to average half the maximum
+    const int64_t parts = ((int64_t)max_context_len + 2 * p - 1) / (2 * (int64_t)p);
+    const int64_t items = waves_per_part * (parts < 1 ? 1 : parts);
+    if (items >= kTargetItems) best = p;
+  }
+  return best;
+}
+
+int32_t resolve_partition(int32_t requested, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_len) {
+  if (requested == 0) return auto_partition(num_seqs, hq, hkv, max_len);
+  return requested;
+}
+
+size_t workspace_for(int32_t num_seqs, int32_t hq, int32_t head_dim, int32_t max_len, int32_t part) {
+  const int64_t max_parts = ((int64_t)max_len + part - 1) / part;
+  if (max_parts <= 1) return 0;
+  return (size_t)num_seqs * hq * max_parts * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null pointer argument";
+    case PKV_ERR_DTYPE: return "unsupported or mismatched dtype";
+    case PKV_ERR_SHAPE: return "invalid shape or size";
+    case PKV_ERR_UNSUPPORTED: return "unsupported block size or head dim";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                   void* v_cache, const pkv_cache_desc* cache, void* hip_stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+  WriteArgs a{k, v, slot_mapping, num_tokens, k_cache, v_cache, cache->num_blocks, cache->num_kv_heads,
+              cache->head_dim, cache->dtype};
+  return from_hip(launch_kv_write(a, as_stream(hip_stream)));
+}
+
+int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t max_context_len) {
+  return auto_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len);
+}
+
+size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
+      partition_tokens < 0)
+    return 0;
+  const int32_t part = resolve_partition(partition_tokens, num_seqs, num_q_heads, num_kv_heads, max_context_len);
+  if (part <= 0) return 0;
+  return workspace_for(num_seqs, num_q_heads, head_dim, max_context_len, part);
+}
+
+int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                      const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                      int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (max_blocks_per_seq <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
+  if (partition_tokens < 0 || partition_tokens % PKV_BLOCK_SIZE != 0) return PKV_ERR_SHAPE;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  const int32_t part = resolve_partition(partition_tokens, num_seqs, num_q_heads, cache->num_kv_heads,
+                                         max_context_len);
+  const int64_t max_parts64 = max_context_len == 0 ? 1 : ((int64_t)max_context_len + part - 1) / part;
+  const size_t need = workspace_for(num_seqs, num_q_heads, cache->head_dim, max_context_len, part);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.chunk_start = nullptr;
+  const size_t o_bytes = need == 0 ? 0 : need / ((size_t)cache->head_dim + 2) * cache->head_dim;
+  a.part_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.part_ml = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes) : nullptr;
+  a.num_seqs = num_seqs;
+  a.rows_per_seq = 1;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.dtype = cache->dtype;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.partition_tokens = part;
+  a.max_parts = (int32_t)max_parts64;
+  a.scale_log2 = scale * kLog2eHost;
+  return from_hip(launch_decode(a, as_stream(hip_stream)));
+}
+
+int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t chunk_len_max, int32_t num_q_heads,
+                             const int32_t* chunk_start, const void* k_cache, const void* v_cache,
+                             const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, float scale, void* out, void* hip_stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_chunks < 0) return PKV_ERR_SHAPE;
+  if (num_chunks == 0) return PKV_OK;
+  if (!q_chunk || !chunk_start || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return PKV_ERR_NULL;
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (chunk_len_max <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  const float sl2 = scale * kLog2eHost;
+  if (cache->dtype == PKV_DTYPE_BF16) {
+    PrefillArgs a{q_chunk, out, k_cache, v_cache, block_tables, context_lens, chunk_start, num_chunks,
+                  chunk_len_max, num_q_heads, cache->num_kv_heads, cache->head_dim, cache->num_blocks,
+                  max_blocks_per_seq, sl2};
+    return from_hip(launch_prefill_mfma(a, as_stream(hip_stream)));
+  }
+  // float32: every chunk row is a decode query over its causal prefix, one
+  // partition covering the whole table (no workspace)
+  DecodeArgs a{};
+  a.q = q_chunk;
+  a.out = out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.chunk_start = chunk_start;
+  a.num_seqs = num_chunks;
+  a.rows_per_seq = chunk_len_max;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.dtype = cache->dtype;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.partition_tokens = max_blocks_per_seq * PKV_BLOCK_SIZE;
+  a.max_parts = 1;
+  a.scale_log2 = sl2;
+  return from_hip(launch_decode(a, as_stream(hip_stream)));
+}
+
+}  // extern "C"

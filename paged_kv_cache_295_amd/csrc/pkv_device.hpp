@@ -1,0 +1,142 @@
+// Device helpers shared by the gfx950 kernels of libpagedkv: element access for
+// float32 / bfloat16 16-byte chunks, wavefront (64-lane) reductions through DPP,
+// and the exp2-based softmax constants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;  // tokens per cache block
+constexpr float kLog2e = 1.4426950408889634f;
+// Running maxima start at the most negative finite float, so that an
+// all-masked stream rescales by exp2(0) = 1 and never forms inf - inf.
+constexpr float kMaxInit = -3.402823466e38f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+struct alignas(16) Chunk {  // 16 bytes: 8 bf16 or 4 float32
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Chunk load_chunk(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  Chunk c;
+  c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+  return c;
+}
+
+__device__ __forceinline__ void store_chunk(void* p, const Chunk& c) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+}
+
+// bf16 pair in one dword -> two floats (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  static constexpr int kDtype = 0;
+  // partial dot product of a query chunk with a key chunk, accumulated into acc
+  __device__ __forceinline__ static float dot(const Chunk& q, const Chunk& k, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(q.w[i]), __uint_as_float(k.w[i]), acc);
+    return acc;
+  }
+  __device__ __forceinline__ static void widen(const Chunk& c, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(c.w[i]);
+  }
+  __device__ __forceinline__ static Chunk narrow(const float (&f)[4]) {
+    Chunk c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.w[i] = __float_as_uint(f[i]);
+    return c;
+  }
+};
+
+template <>
+struct Elem<__bf16> {
+  static constexpr int kPerChunk = 8;
+  static constexpr int kDtype = 1;
+  __device__ __forceinline__ static float dot(const Chunk& q, const Chunk& k, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w[i]),
+                                            __builtin_bit_cast(bf16x2_t, k.w[i]), acc, false);
+    return acc;
+  }
+  __device__ __forceinline__ static void widen(const Chunk& c, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(c.w[i]);
+      f[2 * i + 1] = bf16_hi(c.w[i]);
+    }
+  }
+  __device__ __forceinline__ static Chunk narrow(const float (&f)[8]) {
+    Chunk c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return c;
+  }
+};
+
+// ---- DPP lane exchanges inside a row of 16 lanes -------------------------
+// quad_perm [1,0,3,2] = lane ^ 1, quad_perm [2,3,0,1] = lane ^ 2,
+// row_half_mirror pairs lane i with 7 - i in each half row, row_mirror pairs
+// lane i with 15 - i.  After the first two steps every lane of a quad holds
+// the quad's value, so the mirrors complete an all-reduce over 8 and 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over groups of kLanes consecutive lanes (kLanes in {1,2,4,8,16}); every
+// lane of a group receives the group's sum.
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (kLanes >= 2) x += dpp_f32<0xB1>(x);
+  if constexpr (kLanes >= 4) x += dpp_f32<0x4E>(x);
+  if constexpr (kLanes >= 8) x += dpp_f32<0x141>(x);
+  if constexpr (kLanes >= 16) x += dpp_f32<0x140>(x);
+  static_assert(kLanes <= 16, "group_sum spans at most one DPP row");
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, shfl_xor_f32(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += shfl_xor_f32(x, m);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  return (T)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+}  // namespace pkv

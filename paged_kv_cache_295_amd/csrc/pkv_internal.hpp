@@ -1,0 +1,82 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+// Arguments here are already validated; launchers only pick an instantiation
+// and size the grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+struct WriteArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slots;
+  int64_t num_tokens;
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+};
+
+// One "query row" is a decode query (rows_per_seq == 1, chunk_start == nullptr)
+// or one row of a prefill chunk (rows_per_seq == chunk_len_max, chunk_start set).
+struct DecodeArgs {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* chunk_start;  // nullptr for decode
+  float* part_o;               // [rows][Hq][max_parts][D] unnormalised partial outputs
+  float* part_ml;              // [rows][Hq][max_parts][2] (running max in log2 units, sum)
+  int32_t num_seqs;
+  int32_t rows_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t partition_tokens;
+  int32_t max_parts;  // partitions the grid covers per query row
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+struct PrefillArgs {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* chunk_start;
+  int32_t num_chunks;
+  int32_t chunk_len_max;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  float scale_log2;
+};
+
+hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+// Returns hipErrorInvalidValue if no instantiation covers the shape.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+
+// Heads processed together by one wave for a GQA group of size g.
+inline int heads_per_wave(int g) {
+  if (g % 8 == 0) return 8;
+  if (g % 4 == 0) return 4;
+  if (g % 2 == 0) return 2;
+  return 1;
+}
+
+}  // namespace pkv

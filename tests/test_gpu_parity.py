@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle on the same seeded inputs.
+
+Bar: cache writes bit-exact over the whole cache (poisoned slots included);
+attention within 1e-5 max row-normwise relative error for float32 inputs and
+2e-2 max absolute error for bf16 inputs (unit-variance values, float32
+accumulation).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_295_amd as pkv
+import workloads
+from tests.gpu_util import DeviceWorkload, bits, device, empty_like_q, to_dev, torch, values
+from workloads import SeqSpec, build
+
+pytestmark = pytest.mark.gpu
+
+F32_REL = 1e-5
+BF16_ABS = 2e-2
+SENTINEL = -1024.0  # exact in bf16 and float32
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_attn(got, ref, dtype, what):
+    if dtype == "f32":
+        err = oracle.max_rownorm_rel_err(got, ref)
+        say(f"{what}: max row-normwise rel err {err:.3e}")
+        assert err <= F32_REL, f"{what}: rel err {err}"
+    else:
+        err = oracle.max_abs_err(got, ref)
+        say(f"{what}: max abs err {err:.3e}")
+        assert err <= BF16_ABS, f"{what}: abs err {err}"
+    assert np.isfinite(got).all()
+
+
+def run_write(dw):
+    w = dw.w
+    pkv.paged_kv_write(dw.new_k, dw.new_v, dw.slots, dw.k_cache, dw.v_cache)
+    torch().cuda.synchronize()
+    ref_k, ref_v = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
+    return ref_k, ref_v
+
+
+def run_decode(dw, partition_tokens=0, max_context_len=None):
+    w = dw.w
+    out = empty_like_q(w.q.shape, w.dtype)
+    pkv.paged_attn_decode(dw.q, dw.k_cache, dw.v_cache, dw.tables, dw.lens, float(w.scale), out,
+                          max_context_len=w.max_context_len if max_context_len is None else max_context_len,
+                          partition_tokens=partition_tokens)
+    torch().cuda.synchronize()
+    return out
+
+
+def run_prefill(dw):
+    w = dw.w
+    out = empty_like_q(w.q_chunk.shape, w.dtype)
+    out.fill_(SENTINEL)  # rows past each chunk must keep it
+    pkv.paged_attn_prefill_chunk(dw.q_chunk, dw.chunk_start, dw.k_cache, dw.v_cache, dw.chunk_tables,
+                                 dw.chunk_lens, float(w.scale), out)
+    torch().cuda.synchronize()
+    return out
+
+
+def write_decode_prefill_vs_oracle(w, what):
+    say(f"[{what}] {w.description}; NB={w.num_blocks}")
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    assert np.array_equal(bits(dw.k_cache), ref_k.view(bits(dw.k_cache).dtype)), f"{what}: K cache bits"
+    assert np.array_equal(bits(dw.v_cache), ref_v.view(bits(dw.v_cache).dtype)), f"{what}: V cache bits"
+    say(f"[{what}] write bit-exact over {ref_k.nbytes * 2 / 1e6:.1f} MB of cache")
+    if w.num_seqs:
+        out = run_decode(dw)
+        ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
+        check_attn(values(out), ref, w.dtype, f"[{what}] decode")
+    if w.num_chunks:
+        out = run_prefill(dw)
+        ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, ref_k, ref_v, w.chunk_tables,
+                                   w.chunk_context_lens, w.scale, w.dtype)
+        got = values(out)
+        for c in range(w.num_chunks):
+            n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+            check_attn(got[c, :n], ref[c, :n], w.dtype, f"[{what}] prefill chunk {c}")
+            assert (got[c, n:] == SENTINEL).all(), "rows past the chunk must not be written"
+    return dw, ref_k, ref_v
+
+
+# ------------------------------------------------------------------ the five serving mixes
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_parity(cfg):
+    w = workloads.make(cfg)
+    write_decode_prefill_vs_oracle(w, f"cfg{cfg}")
+    if cfg == 4:
+        # writes never touch the shared prefix blocks
+        assert set(int(s) // 16 for s in w.slot_mapping).isdisjoint(set(w.shared_blocks.tolist()))
+
+
+# ------------------------------------------------------------------ decode shapes and edges
+
+def small(dtype, hq, hkv, d, lens, seed=1, **kw):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return build(f"small-{dtype}-{hq}-{hkv}-{d}", seed, dtype, hq, hkv, d,
+                 [SeqSpec(L, n_new=1 if L else 0) for L in lens], rng=rng, **kw)
+
+
+SHAPES = [("f32", 8, 8, 64), ("f32", 32, 8, 128), ("bf16", 32, 8, 128), ("bf16", 64, 8, 128), ("bf16", 8, 8, 64),
+          ("bf16", 16, 8, 64), ("bf16", 12, 4, 128), ("bf16", 128, 8, 128), ("f32", 24, 4, 64)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_decode_shapes_and_ragged_lengths(shape):
+    dtype, hq, hkv, d = shape
+    lens = [1, 15, 16, 17, 255, 256, 257, 2048, 2049, 700]
+    w = small(dtype, hq, hkv, d, lens)
+    write_decode_prefill_vs_oracle(w, f"shape {shape}")
+
+
+@pytest.mark.parametrize("part", [0, 256, 512, 2048, 4096])
+def test_decode_partition_sizes(part):
+    w = small("bf16", 32, 8, 128, [3000, 5000, 17, 4097, 8192, 1], seed=3)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
+    check_attn(values(run_decode(dw, partition_tokens=part)), ref, "bf16", f"partition {part}")
+
+
+def test_decode_grid_bound_above_lengths():
+    """max_context_len larger than every context (the binding's default bound) changes nothing."""
+    w = small("bf16", 32, 8, 128, [100, 2000, 33], seed=4, max_blocks=256)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
+    check_attn(values(run_decode(dw, max_context_len=4096, partition_tokens=256)), ref, "bf16", "loose bound")
+
+
+def test_empty_context_gives_zero_and_empty_batch_is_noop():
+    w = small("bf16", 32, 8, 128, [0, 40, 0], seed=5)
+    dw = DeviceWorkload(w)
+    run_write(dw)
+    out = values(run_decode(dw))
+    assert (out[0] == 0).all() and (out[2] == 0).all() and np.isfinite(out[1]).all()
+    t = torch()
+    e = t.empty((0, 32, 128), dtype=t.bfloat16, device=device())
+    pkv.paged_attn_decode(e, dw.k_cache, dw.v_cache, dw.tables[:0], dw.lens[:0], 0.1, e)
+    pkv.paged_kv_write(dw.new_k[:0], dw.new_v[:0], dw.slots[:0], dw.k_cache, dw.v_cache)
+    t.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_returns_value_bits(dtype):
+    """A context of one token returns its V row exactly (weight 2^0 = 1)."""
+    d = 128 if dtype == "bf16" else 64
+    w = small(dtype, 16, 4, d, [1, 1, 1], seed=6)
+    dw = DeviceWorkload(w)
+    run_write(dw)
+    out = bits(run_decode(dw))
+    nb = bits(dw.new_v)
+    for s in range(3):
+        for h in range(16):
+            assert np.array_equal(out[s, h], nb[s, h // 4])
+
+
+def test_decode_deterministic_and_permutation_invariant():
+    w = small("bf16", 32, 8, 128, [1234, 4000, 77, 3000], seed=7, num_blocks=600)
+    dw = DeviceWorkload(w)
+    run_write(dw)
+    a = bits(run_decode(dw, partition_tokens=512))
+    b = bits(run_decode(dw, partition_tokens=512))
+    assert np.array_equal(a, b), "two runs must be bitwise equal"
+    # relabel every physical block and rewrite the tables: identical bits
+    rng = np.random.default_rng(0)
+    pi = rng.permutation(w.num_blocks)
+    t = torch()
+    pi_t = t.from_numpy(pi).to(device())
+    kc2 = t.empty_like(dw.k_cache)
+    vc2 = t.empty_like(dw.v_cache)
+    kc2[pi_t] = dw.k_cache
+    vc2[pi_t] = dw.v_cache
+    dw.k_cache, dw.v_cache = kc2, vc2
+    dw.tables = to_dev(pi[w.block_tables].astype(np.int32), "bf16")
+    c = bits(run_decode(dw, partition_tokens=512))
+    assert np.array_equal(a, c)
+
+
+def test_prefix_sharing_matches_private_copies_bits():
+    """Shared prefix blocks give the same bits as private copies of them."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    seqs = [SeqSpec(512 + int(x), shared_prefix=True) for x in rng.integers(16, 200, size=6)]
+    w = build("shared", 8, "bf16", 32, 8, 128, seqs, shared_prefix_blocks=32, rng=rng)
+    dw = DeviceWorkload(w)
+    run_write(dw)
+    a = bits(run_decode(dw))
+    # give every sequence a private copy of the prefix blocks
+    t = torch()
+    nb = w.num_blocks
+    B = w.num_seqs
+    kc = t.empty((nb + B * 32,) + tuple(dw.k_cache.shape[1:]), dtype=dw.k_cache.dtype, device=device())
+    vc = t.empty_like(kc)
+    kc[:nb] = dw.k_cache
+    vc[:nb] = dw.v_cache
+    tables = w.block_tables.copy()
+    for s in range(B):
+        ids = np.arange(nb + 32 * s, nb + 32 * (s + 1))
+        src = t.from_numpy(w.block_tables[s, :32].astype(np.int64)).to(device())
+        kc[nb + 32 * s: nb + 32 * (s + 1)] = dw.k_cache[src]
+        vc[nb + 32 * s: nb + 32 * (s + 1)] = dw.v_cache[src]
+        tables[s, :32] = ids
+    dw.k_cache, dw.v_cache, dw.tables = kc, vc, to_dev(tables.astype(np.int32), "bf16")
+    b = bits(run_decode(dw))
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ cache write
+
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f32", 8, 64), ("bf16", 2, 64), ("f32", 4, 128)])
+def test_write_bit_exact_with_skipped_rows(dtype, hkv, d):
+    rng = np.random.default_rng(9)
+    nb = 50
+    store = np.uint16 if dtype == "bf16" else np.float32
+    kc = rng.standard_normal((nb, hkv, 16, d), dtype=np.float32)
+    if dtype == "bf16":
+        kc = workloads.f32_to_bf16_bits(kc)
+    vc = kc.copy()
+    slots = rng.choice(nb * 16, size=300, replace=False).astype(np.int32)
+    slots[::7] = -1  # skipped rows
+    nk = rng.standard_normal((300, hkv, d), dtype=np.float32)
+    nv = rng.standard_normal((300, hkv, d), dtype=np.float32)
+    if dtype == "bf16":
+        nk, nv = workloads.f32_to_bf16_bits(nk), workloads.f32_to_bf16_bits(nv)
+    kd, vd = to_dev(kc.astype(store), dtype), to_dev(vc.astype(store), dtype)
+    pkv.paged_kv_write(to_dev(nk, dtype), to_dev(nv, dtype), to_dev(slots, dtype), kd, vd)
+    torch().cuda.synchronize()
+    rk, rv = oracle.kv_write(kc, vc, nk, nv, slots)
+    assert np.array_equal(bits(kd), rk.view(bits(kd).dtype))
+    assert np.array_equal(bits(vd), rv.view(bits(vd).dtype))
+
+
+# ------------------------------------------------------------------ prefill chunks
+
+def chunk_workload(dtype, hq, hkv, d, chunks, seed, cmax=None, extra_decode=()):
+    """chunks: list of (chunk_start, chunk_len)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seqs = [SeqSpec(L) for L in extra_decode]
+    seqs += [SeqSpec(p0 + n, n_new=n, kind="chunk") for p0, n in chunks]
+    return build(f"chunks-{dtype}", seed, dtype, hq, hkv, d, seqs, rng=rng,
+                 chunk_len_max=cmax or max(n for _, n in chunks))
+
+
+PREFILL_CASES = [
+    ("bf16", 32, 8, 128, [(0, 512), (1536, 512)]),
+    ("bf16", 32, 8, 128, [(0, 37), (5, 200), (1000, 130), (17, 1)]),
+    ("bf16", 64, 8, 128, [(100, 300), (0, 64)]),
+    ("bf16", 8, 8, 64, [(33, 129), (0, 250)]),
+    ("bf16", 16, 4, 64, [(64, 64), (3, 100)]),
+    ("bf16", 12, 4, 128, [(7, 90)]),
+    ("f32", 8, 8, 64, [(0, 40), (20, 33)]),
+    ("f32", 32, 8, 128, [(100, 77), (0, 16)]),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}-{c[3]}-{len(c[4])}ch")
+def test_prefill_chunk_parity(case):
+    dtype, hq, hkv, d, chunks = case
+    w = chunk_workload(dtype, hq, hkv, d, chunks, seed=11, cmax=max(n for _, n in chunks) + 3)
+    write_decode_prefill_vs_oracle(w, f"prefill {case}")
+
+
+def test_prefill_last_row_equals_decode():
+    """The last row of a chunk is the decode query of the same position."""
+    w = chunk_workload("bf16", 32, 8, 128, [(300, 200)], seed=12)
+    dw = DeviceWorkload(w)
+    run_write(dw)
+    pf = values(run_prefill(dw))[0, 199]
+    t = torch()
+    q = dw.q_chunk[0, 199:200].contiguous()
+    out = t.empty_like(q)
+    pkv.paged_attn_decode(q, dw.k_cache, dw.v_cache, dw.chunk_tables, dw.chunk_lens, float(w.scale), out)
+    t.cuda.synchronize()
+    # different kernels (MFMA with bf16 P vs. vector path): both within tolerance of each other
+    assert oracle.max_abs_err(values(out)[0], pf) <= BF16_ABS
