@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--cold", action="store_true", help="overwrite 512 MB before every step (LLC-cold timing)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="after timing, run one device copy of this many MiB (calibrates HBM byte counters)")
     return p.parse_args()
 
 
@@ -172,6 +174,14 @@ def main():
                           "tflops": round(flops / (pm * 1e-3) / 1e12, 2),
                           "mfma_frac_of_bf16_peak": round(flops / (pm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, cfg)
     print(json.dumps(res), flush=True)

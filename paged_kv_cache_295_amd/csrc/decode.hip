@@ -26,9 +26,10 @@
 //    group of LPT lanes keeps its own running max / sum / output for its
 //    tokens, so no cross-lane traffic is needed per block; the 64 / LPT
 //    streams are merged once at the end of the partition.
-//  * Block tables are read 64 entries at a time into a lane-indexed register
-//    and broadcast with readlane; the next block's K/V loads are issued
-//    before the current block is computed (register double buffering).
+//  * Block-table entries are read with scalar loads; the next block's K/V
+//    loads are issued before the current block is computed (two register
+//    stages).  The rescale of the running output is lazy: only when a score
+//    exceeds the running max by more than 2^8.
 //  * A row whose context fits one partition writes its output directly;
 //    otherwise each partition writes (m, l, unnormalised o) and the merge
 //    kernel combines them: M = max m_p, out = sum 2^(m_p - M) o_p / sum
@@ -78,7 +79,93 @@ struct DecodeShape {
   static_assert(kBlock % kTPP == 0, "a block must be a whole number of passes");
 };
 
-template <typename T, int D, int GB, int LPT>
+#ifndef PKV_DECODE_STREAM_KV
+#define PKV_DECODE_STREAM_KV 1
+#endif
+// K/V tiles are read with the non-temporal (streaming) hint.
+constexpr bool kStreamKV = PKV_DECODE_STREAM_KV != 0;
+
+// Probability-weighted sum of V rows for the tokens a lane holds:
+// acc[h][c][e] += sum_p prob[p][h] * V[p][c][e].  float32 uses plain FMAs; bf16
+// rounds the probabilities to bf16 and pairs two tokens per v_dot2_f32_bf16
+// (the matrix-core prefill rounds P the same way), which halves the ALU work
+// of the PV product.
+template <typename T, int NP, int CPL, int GB>
+struct PV;
+
+template <int NP, int CPL, int GB>
+struct PV<float, NP, CPL, GB> {
+  __device__ __forceinline__ static void apply(const float (&prob)[NP][GB], const Chunk (&vv)[NP][CPL],
+                                               float (&acc)[GB][CPL][4]) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int h = 0; h < GB; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[h][c][e] = fmaf(prob[p][h], __uint_as_float(vv[p][c].w[e]), acc[h][c][e]);
+  }
+};
+
+template <int NP, int CPL, int GB>
+struct PV<__bf16, NP, CPL, GB> {
+  static_assert(NP % 2 == 0, "tokens are paired");
+  __device__ __forceinline__ static void apply(const float (&prob)[NP][GB], const Chunk (&vv)[NP][CPL],
+                                               float (&acc)[GB][CPL][8]) {
+#pragma unroll
+    for (int p = 0; p < NP; p += 2) {
+      bf16x2_t pp[GB];
+#pragma unroll
+      for (int h = 0; h < GB; ++h) pp[h] = __builtin_bit_cast(bf16x2_t, pack_bf16x2(prob[p][h], prob[p + 1][h]));
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t a0 = vv[p][c].w[w], a1 = vv[p + 1][c].w[w];
+          // (token p, token p+1) pairs of dims 2w and 2w+1
+          const bf16x2_t ev = __builtin_bit_cast(bf16x2_t, (a0 & 0xffffu) | (a1 << 16));
+          const bf16x2_t od = __builtin_bit_cast(bf16x2_t, (a0 >> 16) | (a1 & 0xffff0000u));
+#pragma unroll
+          for (int h = 0; h < GB; ++h) {
+            acc[h][c][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], ev, acc[h][c][2 * w], false);
+            acc[h][c][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], od, acc[h][c][2 * w + 1], false);
+          }
+        }
+    }
+  }
+};
+
+// All-reduce every score over the LPT lanes of its token, one DPP step at a
+// time across all scores so that consecutive DPP reads never depend on the
+// instruction right before them.
+template <int LPT, int N>
+__device__ __forceinline__ void group_sum_all(float (&x)[N]) {
+  if constexpr (LPT >= 2) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<0xB1>(x[i]);
+  }
+  if constexpr (LPT >= 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<0x4E>(x[i]);
+  }
+  if constexpr (LPT >= 8) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<0x141>(x[i]);
+  }
+  if constexpr (LPT >= 16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<0x140>(x[i]);
+  }
+}
+
+// A running max is only moved (and the accumulators rescaled) when a new
+// score exceeds it by more than this many powers of two; otherwise the stale
+// max is kept, which bounds every probability by 2^kRescaleSlack and is exact
+// after the final normalisation.
+constexpr float kRescaleSlack = 8.0f;
+
+template <typename T, int D, int GB, int LPT, int NS>
 __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a) {
   using S = DecodeShape<T, D, GB, LPT>;
   using E = typename S::E;
@@ -117,6 +204,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
   const int nparts = (keys + P - 1) / P;
   const int blk0 = start / kBlock;
   const int nblk = (end - start + kBlock - 1) / kBlock;
+  const int nfull = (end - start) / kBlock;  // blocks with no token past `end`
 
   // query chunks for the GB heads, in registers for the whole partition
   Chunk qv[GB][CPL];
@@ -145,18 +233,11 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
   const int64_t tile_bytes = (int64_t)kBlock * D * sizeof(T);
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
   // byte offset of this lane's chunk (pass p, chunk c) inside a tile
-  auto lane_off = [&](int p, int c) -> int {
-    return (p * TPP + tg) * (D * (int)sizeof(T)) + (c * LPT + li) * 16;
-  };
+  const int lane_base = tg * (D * (int)sizeof(T)) + li * 16;
 
-  int tab_reg = 0;  // lane k holds table entry (window base + k)
   bool bad_block = false;
-  auto block_ptr_off = [&](int jb) -> int64_t {
-    if ((jb & 63) == 0) {
-      const int n = nblk - jb;
-      tab_reg = lane < n ? table[jb + lane] : 0;
-    }
-    int p = __builtin_amdgcn_readlane(tab_reg, jb & 63);
+  auto block_off = [&](int jb) -> int64_t {
+    int p = table[jb];  // uniform: a scalar load
     if (p < 0 || p >= a.num_blocks) {
       bad_block = true;
       p = 0;
@@ -164,32 +245,28 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
     return (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
   };
 
-  Chunk kA[NP][CPL], vA[NP][CPL], kB[NP][CPL], vB[NP][CPL];
+  // Every block is loaded whole (rows past `end` in the last block are still
+  // inside that block): one constant per-lane offset plus immediates, so no
+  // address arithmetic sits between the loads of consecutive blocks.
   auto load = [&](Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], int64_t off) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) kk[p][c] = load_chunk(kc + off + lane_off(p, c));
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) vv[p][c] = load_chunk(vc + off + lane_off(p, c));
+      for (int c = 0; c < CPL; ++c) {
+        const int o = lane_base + p * TPP * (D * (int)sizeof(T)) + c * LPT * 16;
+        if constexpr (kStreamKV) {
+          kk[p][c] = load_chunk_stream(kc + off + o);
+          vv[p][c] = load_chunk_stream(vc + off + o);
+        } else {
+          kk[p][c] = load_chunk(kc + off + o);
+          vv[p][c] = load_chunk(vc + off + o);
+        }
+      }
   };
 
   const float sl2 = a.scale_log2;
-  auto compute = [&](Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], int jb) {
-    const int tok0 = (blk0 + jb) * kBlock + tg;  // this lane's token of pass 0
-    const bool tail = (blk0 + jb + 1) * kBlock > end;
-    if (tail) {
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-        if (tok0 + p * TPP >= end)
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) kk[p][c].w[w] = vv[p][c].w[w] = 0u;
-    }
-    float sc[NP][GB];
+  auto compute = [&](const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL], int jb) {
+    float x[NP * GB];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -197,56 +274,99 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
         float d = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) d = E::dot(qv[h][c], kk[p][c], d);
-        sc[p][h] = group_sum<LPT>(d) * sl2;
+        x[p * GB + h] = d;
       }
-    if (tail) {
+    group_sum_all<LPT>(x);
+    float sc[NP][GB];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int h = 0; h < GB; ++h) sc[p][h] = x[p * GB + h] * sl2;
+    {
+      const int tok0 = (blk0 + jb) * kBlock + tg;
 #pragma unroll
       for (int p = 0; p < NP; ++p)
-        if (tok0 + p * TPP >= end)
 #pragma unroll
-          for (int h = 0; h < GB; ++h) sc[p][h] = -__builtin_inff();
+        for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? sc[p][h] : -__builtin_inff();
+    }
+    bool need = false;
+    float bm[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      bm[h] = sc[0][h];
+#pragma unroll
+      for (int p = 1; p < NP; ++p) bm[h] = fmaxf(bm[h], sc[p][h]);
+      need |= bm[h] > m[h] + kRescaleSlack;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const float mn = fmaxf(m[h], bm[h]);
+        const float alpha = fast_exp2(m[h] - mn);
+        m[h] = mn;
+        l[h] *= alpha;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[h][c][e] *= alpha;
+      }
     }
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
-      float bm = sc[0][h];
-#pragma unroll
-      for (int p = 1; p < NP; ++p) bm = fmaxf(bm, sc[p][h]);
-      const float mn = fmaxf(m[h], bm);
-      const float alpha = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      float ls = l[h] * alpha;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][c][e] *= alpha;
+      float ls = l[h];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const float pr = fast_exp2(sc[p][h] - mn);
+        const float pr = fast_exp2(sc[p][h] - m[h]);
         sc[p][h] = pr;
         ls += pr;
       }
       l[h] = ls;
     }
+    // Rows past `end` (only in the last block) may hold NaN: a zero weight is
+    // not enough (0 * NaN), so their V words are replaced by 0.  Done with
+    // selects on every block so that there is a single code path.
+    {
+      const int tok0 = (blk0 + jb) * kBlock + tg;
+      Chunk vz[NP][CPL];
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+      for (int p = 0; p < NP; ++p) {
+        const bool ok = tok0 + p * TPP < end;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        float vf[EPC];
-        E::widen(vv[p][c], vf);
+        for (int c = 0; c < CPL; ++c)
 #pragma unroll
-        for (int h = 0; h < GB; ++h)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[h][c][e] = fmaf(sc[p][h], vf[e], acc[h][c][e]);
+          for (int w = 0; w < 4; ++w) vz[p][c].w[w] = ok ? vv[p][c].w[w] : 0u;
       }
+      PV<T, NP, CPL, GB>::apply(sc, vz, acc);
+    }
   };
 
-  load(kA, vA, block_ptr_off(0));
-  for (int jb = 0; jb < nblk; jb += 2) {
-    if (jb + 1 < nblk) load(kB, vB, block_ptr_off(jb + 1));
-    compute(kA, vA, jb);
-    if (jb + 1 >= nblk) break;
-    if (jb + 2 < nblk) load(kA, vA, block_ptr_off(jb + 2));
-    compute(kB, vB, jb + 1);
+  // NS register stages: while block jb is computed, blocks jb+1 .. jb+NS-1
+  // are in flight and block jb+NS is issued right after.  The prologue fills
+  // every stage so that the loop is entered in its steady state; past the end
+  // loads re-read the last block (an L2 hit), so no load is conditional.  The
+  // body computes NS blocks and exits only at its end (a single exit keeps the
+  // accumulators in place); blocks past the last one are wholly masked and add
+  // exactly nothing.  Table entries are fetched one pass ahead.
+  Chunk kS[NS][NP][CPL], vS[NS][NP][CPL];
+  const int last = nblk - 1;
+  int64_t offs[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    load(kS[st], vS[st], block_off(min(st, last)));
+    // each stage's loads are issued before the next stage's: waits are in order
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int st = 0; st < NS; ++st) offs[st] = block_off(min(NS + st, last));
+  for (int jb = 0;; jb += NS) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      compute(kS[st], vS[st], jb + st);
+      const int64_t next = block_off(min(jb + 2 * NS + st, last));
+      load(kS[st], vS[st], offs[st]);
+      offs[st] = next;
+    }
+    if (jb + NS >= nblk) break;
   }
 
   // merge the 64 / LPT per-token-group streams
@@ -295,7 +415,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
 #pragma unroll
         for (int e4 = 0; e4 < EPC; e4 += 4) {
           float4 v4;
-          v4.x = bad_block ? nan : acc[h][c][e4];
+          v4.x = acc[h][c][e4];
           v4.y = acc[h][c][e4 + 1];
           v4.z = acc[h][c][e4 + 2];
           v4.w = acc[h][c][e4 + 3];
@@ -346,15 +466,38 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   for (int k = 0; k < PER; ++k) outp[lane + k * kWave] = (T)(o[k] * inv);
 }
 
+// Lanes per token: fewer lanes per token means fewer DPP reduction steps and
+// less redundant softmax work per block, at the price of more accumulator
+// registers per lane (head_dim / LPT floats per head).  8 for up to four heads
+// per wave, 16 for eight (whose accumulators would not fit otherwise).
+#ifndef PKV_DECODE_LPT_SMALL_GROUP
+#define PKV_DECODE_LPT_SMALL_GROUP 8
+#endif
+#ifndef PKV_DECODE_STAGES
+#define PKV_DECODE_STAGES 2
+#endif
+template <typename T, int D, int GB>
+constexpr int lanes_per_token() {
+  constexpr int row_chunks = D * (int)sizeof(T) / 16;
+  constexpr int want = GB >= 8 ? 16 : PKV_DECODE_LPT_SMALL_GROUP;
+  return row_chunks < want ? row_chunks : want;
+}
+// Register stages of the K/V prefetch pipeline.
+template <typename T, int D, int GB>
+constexpr int pipeline_stages() {
+  return PKV_DECODE_STAGES;
+}
+
 template <typename T, int D, int GB>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int LPT = (D * (int)sizeof(T) / 16) >= 16 ? 16 : (D * (int)sizeof(T) / 16);
+  constexpr int LPT = lanes_per_token<T, D, GB>();
+  constexpr int NS = pipeline_stages<T, D, GB>();
   const int64_t rows = (int64_t)a.num_seqs * a.rows_per_seq;
   const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
   const int64_t items = rows * a.num_kv_heads * hsubs * a.max_parts;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, GB, LPT>), dim3((unsigned)items), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, GB, LPT, NS>), dim3((unsigned)items), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   const int64_t merges = rows * a.num_q_heads;
