@@ -46,7 +46,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama3-8b-decode", choices=sorted(WORKLOADS))
-    p.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = automatic)")
+    p.add_argument("--partition", type=int, default=0,
+                   help="decode partition tokens (0 = balanced split over a fixed number of wavefronts)")
     p.add_argument("--cold", action="store_true", help="overwrite 512 MB before every step (LLC-cold timing)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
@@ -91,8 +92,7 @@ def main():
         qc, cstart, ctables, clens = (to_dev(w.q_chunk), to_dev(w.chunk_start), to_dev(w.chunk_tables),
                                       to_dev(w.chunk_context_lens))
         oc = torch.empty_like(qc)
-    part = args.partition or pkv.decode_partition_tokens(w.num_seqs, w.num_q_heads, w.num_kv_heads,
-                                                         w.max_context_len)
+    part = args.partition  # 0: balanced split
     ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                           w.max_context_len, part)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -158,7 +158,9 @@ def main():
         "config": {"workload": w.name, "description": w.description, "seed": w.seed, "num_seqs": w.num_seqs,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": 16, "num_blocks": w.num_blocks, "context_tokens": int(w.context_lens.sum()),
-                   "max_context_len": w.max_context_len, "partition_tokens": part,
+                   "max_context_len": w.max_context_len,
+                   "split": f"fixed partitions of {part} tokens" if part else
+                            f"balanced over {pkv.decode_split_waves()} wavefronts",
                    "kv_bytes_per_step": kv_bytes, "llc": "cold (512 MB overwrite per step)" if args.cold else "warm",
                    "layers_per_step": 1},
         "seq_tokens_per_s": round(seq_tok_s, 1),

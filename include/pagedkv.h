@@ -92,19 +92,24 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
                    void* k_cache, void* v_cache, const pkv_cache_desc* cache, void* hip_stream);
 
 /*
- * Split-context decode: a sequence's context is cut into partitions of
- * `partition_tokens` tokens (a multiple of 16); each partition's running max,
- * sum of exponentials and unnormalised output are combined by a log-sum-exp
- * merge, which equals the one-pass softmax in exact arithmetic.
+ * Split-context decode.  A sequence's context is cut into pieces; each piece
+ * yields a running max, a sum of exponentials and an unnormalised output, and
+ * a log-sum-exp merge combines the pieces, which equals the one-pass softmax
+ * in exact arithmetic.  Two ways of cutting:
  *
- * paged_attn_decode_partition_tokens returns the partition size used when
- * paged_attn_decode is called with partition_tokens == 0 (a function of the
- * batch shape only).  paged_attn_decode_workspace_bytes returns the workspace
- * paged_attn_decode needs for these sizes (0 if every sequence fits one
- * partition); partition_tokens == 0 means the automatic choice.
+ *   partition_tokens == 0 (recommended): balanced split.  The whole batch's
+ *     work -- every (sequence, kv head, 16-token block) -- is divided into
+ *     paged_attn_decode_split_waves() equal runs of consecutive blocks, one
+ *     per wavefront, so every wavefront reads the same amount of K/V whatever
+ *     the mix of context lengths; a context is cut wherever a run ends.  The
+ *     workspace size does not depend on the context lengths.
+ *   partition_tokens > 0 (a multiple of 16): fixed partitions of that many
+ *     tokens per sequence, one wavefront each.
+ *
+ * paged_attn_decode_workspace_bytes returns the workspace paged_attn_decode
+ * needs for these sizes (0 if none).
  */
-int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                           int32_t max_context_len);
+int32_t paged_attn_decode_split_waves(void);
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_context_len, int32_t partition_tokens);
 
@@ -119,16 +124,20 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *   q, out            [num_seqs][num_q_heads][head_dim]
  *   block_tables      int32 [num_seqs][max_blocks_per_seq]
  *   context_lens      int32 [num_seqs] (device); context_lens[s] == 0 gives out = 0
- *   max_context_len   host-side upper bound of context_lens (sizes the grid)
+ *   max_context_len   host-side upper bound of context_lens (sizes the grid
+ *                     and the workspace of fixed partitions)
  *   scale             softmax scale, usually 1/sqrt(head_dim)
- *   partition_tokens  0 = automatic, else a positive multiple of 16
+ *   partition_tokens  0 = balanced split, else fixed partitions of that many
+ *                     tokens (a positive multiple of 16)
  *   workspace         device scratch of at least
  *                     paged_attn_decode_workspace_bytes(...) bytes (may be
  *                     NULL when that is 0); contents need no initialisation
  *
  * Device-side contract: 0 <= context_lens[s] <= max_context_len and the first
  * ceil(context_lens[s]/16) table entries lie in [0, num_blocks).  A sequence
- * that breaks it gets NaN in every output row of the heads concerned.
+ * that breaks it gets NaN in every output row of the heads concerned (with
+ * fixed partitions a context above max_context_len counts as broken; the
+ * balanced split accepts any context up to 16 * max_blocks_per_seq).
  * num_seqs == 0 is a no-op.
  */
 int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,

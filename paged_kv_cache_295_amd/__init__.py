@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "PagedKVError", "load_library", "paged_kv_write", "paged_attn_decode", "paged_attn_prefill_chunk",
-    "decode_workspace_bytes", "decode_partition_tokens", "library_path", "BLOCK_SIZE",
+    "decode_workspace_bytes", "decode_split_waves", "library_path", "BLOCK_SIZE",
 ]
 
 BLOCK_SIZE = 16
@@ -56,8 +56,8 @@ def load_library():
     cdp = ctypes.POINTER(CacheDesc)
     lib.paged_kv_write.argtypes = [vp, vp, vp, i64, vp, vp, cdp, vp]
     lib.paged_kv_write.restype = ctypes.c_int
-    lib.paged_attn_decode_partition_tokens.argtypes = [i32, i32, i32, i32]
-    lib.paged_attn_decode_partition_tokens.restype = i32
+    lib.paged_attn_decode_split_waves.argtypes = []
+    lib.paged_attn_decode_split_waves.restype = i32
     lib.paged_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_attn_decode_workspace_bytes.restype = sz
     lib.paged_attn_decode.argtypes = [vp, i32, i32, vp, vp, cdp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp]
@@ -138,9 +138,9 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
     _check(st, "paged_kv_write")
 
 
-def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, max_context_len) -> int:
-    return int(load_library().paged_attn_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads,
-                                                                 max_context_len))
+def decode_split_waves() -> int:
+    """Wavefronts the balanced decode split (partition_tokens=0) divides a batch's work over."""
+    return int(load_library().paged_attn_decode_split_waves())
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
@@ -154,8 +154,9 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     """out[s, h] = softmax(scale q[s, h] K_s^T) V_s over the first context_lens[s] cached tokens.
 
     max_context_len: host-side bound on context_lens (defaults to the block
-    table's capacity, 16 * block_tables.shape[1]).  workspace: optional uint8
-    device tensor; allocated here when needed and not given.
+    table's capacity, 16 * block_tables.shape[1]).  partition_tokens: 0 for the
+    balanced split, else fixed partitions of that many tokens.  workspace:
+    optional uint8 device tensor; allocated here when needed and not given.
     """
     lib = load_library()
     _same_dtype(q, out, k_cache, v_cache)

@@ -25,32 +25,15 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
-constexpr int32_t kMinPartition = 256;
-constexpr int32_t kMaxPartition = 16384;
-// Work items the automatic partition size aims for: about eight waves per
-// compute unit on a 256-CU MI355X.
-constexpr int64_t kTargetItems = 2048;
-
-int32_t auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len) {
-  if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads <= 0) return kMinPartition;
-  const int64_t waves_per_part =
-      (int64_t)num_seqs * num_kv_heads * ((num_q_heads / num_kv_heads) / heads_per_wave(num_q_heads / num_kv_heads));
-  int32_t best = kMinPartition;
-  for (int32_t p = kMinPartition; p <= kMaxPartition; p *= 2) {
-    // contexts are assumed to average half the maximum
-    const int64_t parts = ((int64_t)max_context_len + 2 * p - 1) / (2 * (int64_t)p);
-    const int64_t items = waves_per_part * (parts < 1 ? 1 : parts);
-    if (items >= kTargetItems) best = p;
-  }
-  return best;
+// Balanced split (partition_tokens == 0): kBalancedWaves waves, each with up
+// to two partials of heads_per_wave heads.
+size_t balanced_workspace(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  const int gb = heads_per_wave(num_q_heads / num_kv_heads);
+  return (size_t)kBalancedWaves * 2 * gb * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-int32_t resolve_partition(int32_t requested, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_len) {
-  if (requested == 0) return auto_partition(num_seqs, hq, hkv, max_len);
-  return requested;
-}
-
-size_t workspace_for(int32_t num_seqs, int32_t hq, int32_t head_dim, int32_t max_len, int32_t part) {
+// Fixed partitions of `part` tokens: one partial per (row, head, partition).
+size_t partition_workspace(int32_t num_seqs, int32_t hq, int32_t head_dim, int32_t max_len, int32_t part) {
   const int64_t max_parts = ((int64_t)max_len + part - 1) / part;
   if (max_parts <= 1) return 0;
   return (size_t)num_seqs * hq * max_parts * ((size_t)head_dim + 2) * sizeof(float);
@@ -87,19 +70,15 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
   return from_hip(launch_kv_write(a, as_stream(hip_stream)));
 }
 
-int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                           int32_t max_context_len) {
-  return auto_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len);
-}
+int32_t paged_attn_decode_split_waves(void) { return kBalancedWaves; }
 
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
-      partition_tokens < 0)
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_tokens < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  const int32_t part = resolve_partition(partition_tokens, num_seqs, num_q_heads, num_kv_heads, max_context_len);
-  if (part <= 0) return 0;
-  return workspace_for(num_seqs, num_q_heads, head_dim, max_context_len, part);
+  if (partition_tokens == 0) return balanced_workspace(num_q_heads, num_kv_heads, head_dim);
+  return partition_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens);
 }
 
 int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache, const void* v_cache,
@@ -113,13 +92,16 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
   if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (max_blocks_per_seq <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
   if (partition_tokens < 0 || partition_tokens % PKV_BLOCK_SIZE != 0) return PKV_ERR_SHAPE;
   if (!isfinite(scale)) return PKV_ERR_SHAPE;
-  const int32_t part = resolve_partition(partition_tokens, num_seqs, num_q_heads, cache->num_kv_heads,
-                                         max_context_len);
-  const int64_t max_parts64 = max_context_len == 0 ? 1 : ((int64_t)max_context_len + part - 1) / part;
-  const size_t need = workspace_for(num_seqs, num_q_heads, cache->head_dim, max_context_len, part);
+  const bool balanced = partition_tokens == 0;
+  const int32_t part = balanced ? max_blocks_per_seq * PKV_BLOCK_SIZE : partition_tokens;
+  const int64_t max_parts64 = balanced || max_context_len == 0 ? 1 : ((int64_t)max_context_len + part - 1) / part;
+  if (max_parts64 > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  const size_t need = balanced ? balanced_workspace(num_q_heads, cache->num_kv_heads, cache->head_dim)
+                               : partition_workspace(num_seqs, num_q_heads, cache->head_dim, max_context_len, part);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   DecodeArgs a{};
   a.q = q;
@@ -143,6 +125,7 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
   a.partition_tokens = part;
   a.max_parts = (int32_t)max_parts64;
   a.scale_log2 = scale * kLog2eHost;
+  a.balanced_waves = balanced ? kBalancedWaves : 0;
   return from_hip(launch_decode(a, as_stream(hip_stream)));
 }
 

@@ -165,17 +165,249 @@ __device__ __forceinline__ void group_sum_all(float (&x)[N]) {
 // after the final normalisation.
 constexpr float kRescaleSlack = 8.0f;
 
+// One wave's attention state for GB query heads of one kv head over a run of
+// consecutive blocks of one sequence (a "segment"): the query chunks, and per
+// token group the running max m (log2 units), sum l and unnormalised output.
 template <typename T, int D, int GB, int LPT, int NS>
-__global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a) {
+struct Segment {
   using S = DecodeShape<T, D, GB, LPT>;
   using E = typename S::E;
-  constexpr int EPC = S::kEPC, CPL = S::kCPL, TPP = S::kTPP, NP = S::kNPass;
+  static constexpr int EPC = S::kEPC, CPL = S::kCPL, TPP = S::kTPP, NP = S::kNPass;
 
+  Chunk qv[GB][CPL];
+  float m[GB], l[GB], acc[GB][CPL][EPC];
+  bool bad_block;
+  int tg, li;
+
+  __device__ __forceinline__ Segment() {
+    const int lane = __lane_id();
+    tg = lane / LPT;
+    li = lane % LPT;
+  }
+
+  // Attend the GB query rows at qrow (head h0 of the row) over tokens
+  // [16 * blk0, end) of one sequence, whose blocks blk0 .. blk0 + nblk - 1 are
+  // listed at table[0 .. nblk - 1], for kv head g.
+  __device__ __forceinline__ void run(const DecodeArgs& a, const T* __restrict__ qrow,
+                                      const int32_t* __restrict__ table, int g, int blk0, int nblk, int end) {
+#pragma unroll
+    for (int h = 0; h < GB; ++h)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) qv[h][c] = load_chunk(qrow + h * D + (c * LPT + li) * EPC);
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      m[h] = kMaxInit;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][c][e] = 0.0f;
+    }
+    bad_block = false;
+
+    const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache);
+    const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache);
+    const int64_t tile_bytes = (int64_t)kBlock * D * sizeof(T);
+    const int64_t blk_stride = tile_bytes * a.num_kv_heads;
+    const int num_blocks = a.num_blocks;
+    // byte offset of this lane's chunk (pass p, chunk c) inside a tile
+    const int lane_base = tg * (D * (int)sizeof(T)) + li * 16;
+
+    auto block_off = [&](int jb) -> int64_t {
+      int p = table[jb];  // uniform: a scalar load
+      if (p < 0 || p >= num_blocks) {
+        bad_block = true;
+        p = 0;
+      }
+      return (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
+    };
+
+    // Every block is loaded whole (rows past `end` in the last block are still
+    // inside that block): one constant per-lane offset plus immediates, so no
+    // address arithmetic sits between the loads of consecutive blocks.
+    auto load = [&](Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], int64_t off) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int o = lane_base + p * TPP * (D * (int)sizeof(T)) + c * LPT * 16;
+          if constexpr (kStreamKV) {
+            kk[p][c] = load_chunk_stream(kc + off + o);
+            vv[p][c] = load_chunk_stream(vc + off + o);
+          } else {
+            kk[p][c] = load_chunk(kc + off + o);
+            vv[p][c] = load_chunk(vc + off + o);
+          }
+        }
+    };
+
+    const float sl2 = a.scale_log2;
+    auto compute = [&](const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL], int jb) {
+      float x[NP * GB];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+          float d = 0.0f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) d = E::dot(qv[h][c], kk[p][c], d);
+          x[p * GB + h] = d;
+        }
+      group_sum_all<LPT>(x);
+      const int tok0 = (blk0 + jb) * kBlock + tg;  // this lane's token of pass 0
+      float sc[NP][GB];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? x[p * GB + h] * sl2 : -__builtin_inff();
+      bool need = false;
+      float bm[GB];
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        bm[h] = sc[0][h];
+#pragma unroll
+        for (int p = 1; p < NP; ++p) bm[h] = fmaxf(bm[h], sc[p][h]);
+        need |= bm[h] > m[h] + kRescaleSlack;
+      }
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+          const float mn = fmaxf(m[h], bm[h]);
+          const float alpha = fast_exp2(m[h] - mn);
+          m[h] = mn;
+          l[h] *= alpha;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[h][c][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        float ls = l[h];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const float pr = fast_exp2(sc[p][h] - m[h]);
+          sc[p][h] = pr;
+          ls += pr;
+        }
+        l[h] = ls;
+      }
+      // Rows past `end` may hold NaN: a zero weight is not enough (0 * NaN), so
+      // their V words are replaced by 0.  Selects on every block keep a single
+      // code path.
+      Chunk vz[NP][CPL];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const bool ok = tok0 + p * TPP < end;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vz[p][c].w[w] = ok ? vv[p][c].w[w] : 0u;
+      }
+      PV<T, NP, CPL, GB>::apply(sc, vz, acc);
+    };
+
+    // NS register stages: while block jb is computed, blocks jb+1 .. jb+NS-1
+    // are in flight and block jb+NS is issued right after.  The prologue fills
+    // every stage so that the loop is entered in its steady state; past the end
+    // loads re-read the last block (an L2 hit), so no load is conditional.  The
+    // body computes NS blocks and exits only at its end (a single exit keeps the
+    // accumulators in place); blocks past the last one lie wholly past `end`,
+    // are masked and add exactly nothing.  Table entries are fetched one pass
+    // ahead.
+    Chunk kS[NS][NP][CPL], vS[NS][NP][CPL];
+    const int last = nblk - 1;
+    int64_t offs[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      load(kS[st], vS[st], block_off(min(st, last)));
+      // each stage's loads are issued before the next stage's: waits are in order
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) offs[st] = block_off(min(NS + st, last));
+    for (int jb = 0;; jb += NS) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        compute(kS[st], vS[st], jb + st);
+        const int64_t next = block_off(min(jb + 2 * NS + st, last));
+        load(kS[st], vS[st], offs[st]);
+        offs[st] = next;
+      }
+      if (jb + NS >= nblk) break;
+    }
+  }
+
+  // Combine the 64 / LPT token-group streams (every lane ends with the totals):
+  // agree on the largest running max, rescale to it, then add.
+  __device__ __forceinline__ void merge_groups() {
+    static_assert(LPT == 8 || LPT == 16, "token groups differ in lane bits 3..5 or 4..5");
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      const float M = groups_max<LPT>(m[h]);
+      const float f = fast_exp2(m[h] - M);
+      m[h] = M;
+      l[h] = groups_add<LPT>(l[h] * f);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][c][e] = groups_add<LPT>(acc[h][c][e] * f);
+    }
+  }
+
+  // Normalised output of the GB heads at outp (head h0 of the row).
+  __device__ __forceinline__ void store_out(T* __restrict__ outp) const {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      if (tg != h % TPP) continue;
+      const float inv = bad_block ? nan : 1.0f / l[h];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        float o[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) o[e] = acc[h][c][e] * inv;
+        store_chunk(outp + h * D + (c * LPT + li) * EPC, E::narrow(o));
+      }
+    }
+  }
+
+  // Partial (m, l, unnormalised o) of head h at po + h * ostride (D floats) and
+  // pml + h * mlstride (2 floats).
+  __device__ __forceinline__ void store_partial(float* __restrict__ po, int64_t ostride, float* __restrict__ pml,
+                                                int64_t mlstride) const {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      if (tg != h % TPP) continue;
+      float* o = po + h * ostride;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e4 = 0; e4 < EPC; e4 += 4) {
+          float4 v4;
+          v4.x = acc[h][c][e4];
+          v4.y = acc[h][c][e4 + 1];
+          v4.z = acc[h][c][e4 + 2];
+          v4.w = acc[h][c][e4 + 3];
+          *reinterpret_cast<float4*>(o + (c * LPT + li) * EPC + e4) = v4;
+        }
+      if (li == 0) {
+        pml[h * mlstride] = bad_block ? nan : m[h];
+        pml[h * mlstride + 1] = l[h];
+      }
+    }
+  }
+};
+
+// Fixed partitions: one wave per (query row, kv head, head subgroup,
+// partition of P tokens).  Also serves float32 prefill rows (one partition
+// covering the whole table).
+template <typename T, int D, int GB, int LPT, int NS>
+__global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a) {
   const int lane = __lane_id();
-  const int tg = lane / LPT;
-  const int li = lane % LPT;
   const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
-
   int64_t t = blockIdx.x;
   const int part = (int)(t % a.max_parts);
   t /= a.max_parts;
@@ -204,228 +436,17 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
   const int nparts = (keys + P - 1) / P;
   const int blk0 = start / kBlock;
   const int nblk = (end - start + kBlock - 1) / kBlock;
-  const int nfull = (end - start) / kBlock;  // blocks with no token past `end`
 
-  // query chunks for the GB heads, in registers for the whole partition
-  Chunk qv[GB][CPL];
-  {
-    const T* qrow = reinterpret_cast<const T*>(a.q) + (row * a.num_q_heads + h0) * (int64_t)D;
-#pragma unroll
-    for (int h = 0; h < GB; ++h)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) qv[h][c] = load_chunk(qrow + h * D + (c * LPT + li) * EPC);
-  }
-
-  float m[GB], l[GB], acc[GB][CPL][EPC];
-#pragma unroll
-  for (int h = 0; h < GB; ++h) {
-    m[h] = kMaxInit;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[h][c][e] = 0.0f;
-  }
-
-  const int32_t* __restrict__ table = a.block_tables + (int64_t)ri.seq * a.max_blocks_per_seq + blk0;
-  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache);
-  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache);
-  const int64_t tile_bytes = (int64_t)kBlock * D * sizeof(T);
-  const int64_t blk_stride = tile_bytes * a.num_kv_heads;
-  // byte offset of this lane's chunk (pass p, chunk c) inside a tile
-  const int lane_base = tg * (D * (int)sizeof(T)) + li * 16;
-
-  bool bad_block = false;
-  auto block_off = [&](int jb) -> int64_t {
-    int p = table[jb];  // uniform: a scalar load
-    if (p < 0 || p >= a.num_blocks) {
-      bad_block = true;
-      p = 0;
-    }
-    return (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
-  };
-
-  // Every block is loaded whole (rows past `end` in the last block are still
-  // inside that block): one constant per-lane offset plus immediates, so no
-  // address arithmetic sits between the loads of consecutive blocks.
-  auto load = [&](Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], int64_t off) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int o = lane_base + p * TPP * (D * (int)sizeof(T)) + c * LPT * 16;
-        if constexpr (kStreamKV) {
-          kk[p][c] = load_chunk_stream(kc + off + o);
-          vv[p][c] = load_chunk_stream(vc + off + o);
-        } else {
-          kk[p][c] = load_chunk(kc + off + o);
-          vv[p][c] = load_chunk(vc + off + o);
-        }
-      }
-  };
-
-  const float sl2 = a.scale_log2;
-  auto compute = [&](const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL], int jb) {
-    float x[NP * GB];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int h = 0; h < GB; ++h) {
-        float d = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) d = E::dot(qv[h][c], kk[p][c], d);
-        x[p * GB + h] = d;
-      }
-    group_sum_all<LPT>(x);
-    float sc[NP][GB];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int h = 0; h < GB; ++h) sc[p][h] = x[p * GB + h] * sl2;
-    {
-      const int tok0 = (blk0 + jb) * kBlock + tg;
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? sc[p][h] : -__builtin_inff();
-    }
-    bool need = false;
-    float bm[GB];
-#pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      bm[h] = sc[0][h];
-#pragma unroll
-      for (int p = 1; p < NP; ++p) bm[h] = fmaxf(bm[h], sc[p][h]);
-      need |= bm[h] > m[h] + kRescaleSlack;
-    }
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-#pragma unroll
-      for (int h = 0; h < GB; ++h) {
-        const float mn = fmaxf(m[h], bm[h]);
-        const float alpha = fast_exp2(m[h] - mn);
-        m[h] = mn;
-        l[h] *= alpha;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[h][c][e] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      float ls = l[h];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const float pr = fast_exp2(sc[p][h] - m[h]);
-        sc[p][h] = pr;
-        ls += pr;
-      }
-      l[h] = ls;
-    }
-    // Rows past `end` (only in the last block) may hold NaN: a zero weight is
-    // not enough (0 * NaN), so their V words are replaced by 0.  Done with
-    // selects on every block so that there is a single code path.
-    {
-      const int tok0 = (blk0 + jb) * kBlock + tg;
-      Chunk vz[NP][CPL];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const bool ok = tok0 + p * TPP < end;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) vz[p][c].w[w] = ok ? vv[p][c].w[w] : 0u;
-      }
-      PV<T, NP, CPL, GB>::apply(sc, vz, acc);
-    }
-  };
-
-  // NS register stages: while block jb is computed, blocks jb+1 .. jb+NS-1
-  // are in flight and block jb+NS is issued right after.  The prologue fills
-  // every stage so that the loop is entered in its steady state; past the end
-  // loads re-read the last block (an L2 hit), so no load is conditional.  The
-  // body computes NS blocks and exits only at its end (a single exit keeps the
-  // accumulators in place); blocks past the last one are wholly masked and add
-  // exactly nothing.  Table entries are fetched one pass ahead.
-  Chunk kS[NS][NP][CPL], vS[NS][NP][CPL];
-  const int last = nblk - 1;
-  int64_t offs[NS];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    load(kS[st], vS[st], block_off(min(st, last)));
-    // each stage's loads are issued before the next stage's: waits are in order
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int st = 0; st < NS; ++st) offs[st] = block_off(min(NS + st, last));
-  for (int jb = 0;; jb += NS) {
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      compute(kS[st], vS[st], jb + st);
-      const int64_t next = block_off(min(jb + 2 * NS + st, last));
-      load(kS[st], vS[st], offs[st]);
-      offs[st] = next;
-    }
-    if (jb + NS >= nblk) break;
-  }
-
-  // merge the 64 / LPT per-token-group streams
-#pragma unroll
-  for (int mask = LPT; mask < kWave; mask <<= 1) {
-#pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      const float mo = shfl_xor_f32(m[h], mask);
-      const float lo = shfl_xor_f32(l[h], mask);
-      const float M = fmaxf(m[h], mo);
-      const float fs = fast_exp2(m[h] - M), fo = fast_exp2(mo - M);
-      l[h] = l[h] * fs + lo * fo;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const float ao = shfl_xor_f32(acc[h][c][e], mask);
-          acc[h][c][e] = acc[h][c][e] * fs + ao * fo;
-        }
-      m[h] = M;
-    }
-  }
-
-  const float nan = __builtin_nanf("");
+  Segment<T, D, GB, LPT, NS> seg;
+  const T* qrow = reinterpret_cast<const T*>(a.q) + (row * a.num_q_heads + h0) * (int64_t)D;
+  seg.run(a, qrow, a.block_tables + (int64_t)ri.seq * a.max_blocks_per_seq + blk0, g, blk0, nblk, end);
+  seg.merge_groups();
   if (nparts == 1) {
-#pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      if (tg != h % TPP) continue;
-      const float inv = bad_block ? nan : 1.0f / l[h];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        float o[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) o[e] = acc[h][c][e] * inv;
-        store_chunk(outp + h * D + (c * LPT + li) * EPC, E::narrow(o));
-      }
-    }
+    seg.store_out(outp);
   } else {
-#pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      if (tg != h % TPP) continue;
-      const int64_t pidx = (row * a.num_q_heads + h0 + h) * (int64_t)a.max_parts + part;
-      float* po = a.part_o + pidx * D;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-#pragma unroll
-        for (int e4 = 0; e4 < EPC; e4 += 4) {
-          float4 v4;
-          v4.x = acc[h][c][e4];
-          v4.y = acc[h][c][e4 + 1];
-          v4.z = acc[h][c][e4 + 2];
-          v4.w = acc[h][c][e4 + 3];
-          *reinterpret_cast<float4*>(po + (c * LPT + li) * EPC + e4) = v4;
-        }
-      if (li == 0) {
-        a.part_ml[pidx * 2] = bad_block ? nan : m[h];
-        a.part_ml[pidx * 2 + 1] = l[h];
-      }
-    }
+    const int64_t pidx = (row * a.num_q_heads + h0) * (int64_t)a.max_parts + part;
+    seg.store_partial(a.part_o + pidx * D, (int64_t)a.max_parts * D, a.part_ml + pidx * 2,
+                      (int64_t)a.max_parts * 2);
   }
 }
 
@@ -466,6 +487,239 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   for (int k = 0; k < PER; ++k) outp[lane + k * kWave] = (T)(o[k] * inv);
 }
 
+// ---------------------------------------------------------------- balanced split
+//
+// The work of a decode step is the list of units (sequence s, stream k, block
+// j), streams k = (kv head, head subgroup) of a sequence, ordered by s, then k,
+// then j.  With U units and W waves, wave w takes units [w U / W, (w+1) U / W):
+// every wave reads the same number of K/V blocks (within one) whatever the mix
+// of context lengths, so no compute unit idles behind a long sequence.  A
+// stream wholly inside one wave's range is finished there; a stream cut by a
+// range boundary leaves (m, l, o) partials -- a wave has at most two: its first
+// segment (slot 0) and its last (slot 1) -- which the merge kernel combines.
+//
+// Sequences with a context outside [0, 16 * max_blocks] contribute no units;
+// the merge kernel writes NaN for them (and 0 for an empty context).
+
+__device__ __forceinline__ int seq_blocks(int L, int cap) { return (L >= 0 && L <= cap) ? (L + kBlock - 1) / kBlock : 0; }
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, kCtrl, kRowMask, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (DPP: row_shr within rows of 16,
+// then row_bcast:15 / row_bcast:31 across rows).
+__device__ __forceinline__ int wave_incl_scan_int(int x) {
+  x += dpp_i32<0x111>(x);         // row_shr:1
+  x += dpp_i32<0x112>(x);         // row_shr:2
+  x += dpp_i32<0x114>(x);         // row_shr:4
+  x += dpp_i32<0x118>(x);         // row_shr:8
+  x += dpp_i32<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
+  x += dpp_i32<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan_int(x), kWave - 1);
+}
+
+// Total blocks over all sequences, and the blocks of the sequences before s
+// (every lane gets both); one pass over the lengths.
+__device__ __forceinline__ void block_counts(const int32_t* __restrict__ lens, int B, int s, int cap, int64_t& total,
+                                             int64_t& before) {
+  total = 0;
+  before = 0;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int i = c0 + __lane_id();
+    const int nb = i < B ? seq_blocks(lens[i], cap) : 0;
+    const int incl = wave_incl_scan_int(nb);
+    total += __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (s >= c0 + kWave) {
+      before += __builtin_amdgcn_readlane(incl, kWave - 1);
+    } else if (s > c0) {
+      before += __builtin_amdgcn_readlane(incl, s - c0 - 1);
+    }
+  }
+  total = uniform64(total);
+  before = uniform64(before);
+}
+
+// Total blocks over all sequences (every lane gets it).
+__device__ __forceinline__ int64_t total_blocks(const int32_t* __restrict__ lens, int B, int cap) {
+  int64_t tot = 0, before = 0;
+  block_counts(lens, B, 0, cap, tot, before);
+  return tot;
+}
+
+__device__ __forceinline__ int64_t range_begin(int w, int W, int64_t U) { return (int64_t)w * U / W; }
+// The wave whose range holds unit u.
+__device__ __forceinline__ int wave_of(int64_t u, int W, int64_t U) { return (int)(((u + 1) * W + U - 1) / U) - 1; }
+
+template <typename T, int D, int GB, int LPT, int NS>
+__global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a) {
+  const int lane = __lane_id();
+  const int W = gridDim.x;
+  const int w = blockIdx.x;
+  const int B = a.num_seqs;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int hsubs = G / GB;
+  const int HH = a.num_kv_heads * hsubs;  // streams per sequence
+  const int cap = a.max_blocks_per_seq * kBlock;
+  const int32_t* __restrict__ lens = a.context_lens;
+
+  const int64_t U = total_blocks(lens, B, cap) * HH;
+  const int64_t u0 = range_begin(w, W, U), u1 = range_begin(w + 1, W, U);
+  if (u0 >= u1) return;
+
+  // locate u0: the sequence s whose units [HH cum, HH (cum + nb)) hold it
+  int s = 0;
+  int64_t cum = 0;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int i = c0 + lane;
+    const int nb = i < B ? seq_blocks(lens[i], cap) : 0;
+    const int incl = wave_incl_scan_int(nb);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && (cum + incl) * HH > u0);
+    if (hit) {
+      const int ln = __builtin_ctzll(hit);
+      s = c0 + ln;
+      cum += __builtin_amdgcn_readlane(incl - nb, ln);
+      break;
+    }
+    cum += __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  s = __builtin_amdgcn_readfirstlane(s);
+  cum = uniform64(cum);
+
+  Segment<T, D, GB, LPT, NS> seg;
+  int L = __builtin_amdgcn_readfirstlane(lens[s]);
+  int nb = seq_blocks(L, cap);
+  for (int64_t u = u0;;) {
+    const int r = (int)(u - cum * HH);  // unit offset inside sequence s
+    const int k = r / nb, j = r - k * nb;
+    const int g = k / hsubs, hs = k - g * hsubs;
+    const int64_t seg_end = min(u1, cum * HH + (int64_t)(k + 1) * nb);
+    const int jn = j + (int)(seg_end - u);
+    const int h0 = g * G + hs * GB;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)s * a.num_q_heads + h0) * D;
+    seg.run(a, qrow, a.block_tables + (int64_t)s * a.max_blocks_per_seq + j, g, j, jn - j, min(L, jn * kBlock));
+    seg.merge_groups();
+    if (j == 0 && jn == nb) {
+      seg.store_out(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D);
+    } else {
+      const int64_t slot = (int64_t)w * 2 + (u == u0 ? 0 : 1);
+      seg.store_partial(a.part_o + slot * GB * D, D, a.part_ml + slot * GB * 2, 2);
+    }
+    u = seg_end;
+    if (u >= u1) break;
+    if (k + 1 == HH) {  // next sequence that has blocks (one exists: u < U)
+      cum += nb;
+      do {
+        ++s;
+        L = __builtin_amdgcn_readfirstlane(lens[s]);
+        nb = seq_blocks(L, cap);
+      } while (nb == 0);
+    }
+  }
+}
+
+// One wave per (sequence, stream): writes NaN / 0 for sequences with an
+// invalid / empty context, and merges the partials of a stream that was cut
+// across wave ranges.  The loads are issued together, not one owner after the
+// other: lane j examines candidate wave wf + j (the owners of a stream are
+// consecutive waves, except for empty ranges when waves outnumber units) and
+// loads its (m, l) for every head; the outputs then sum over the owners with
+// lane k owning dims k, k + 64, ...
+template <typename T, int D, int GB>
+__global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeArgs a, int W) {
+  constexpr int PER = D / kWave;
+  const int lane = __lane_id();
+  const int B = a.num_seqs;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int hsubs = G / GB;
+  const int HH = a.num_kv_heads * hsubs;
+  const int cap = a.max_blocks_per_seq * kBlock;
+  const int s = blockIdx.x / HH;
+  const int k = blockIdx.x - s * HH;
+  const int g = k / hsubs, hs = k - g * hsubs;
+  const int h0 = g * G + hs * GB;
+  T* outp = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D;
+
+  const int L = a.context_lens[s];
+  int64_t total, before;
+  block_counts(a.context_lens, B, s, cap, total, before);
+  if (L < 0 || L > cap || L == 0) {
+    const float fill = L == 0 ? 0.0f : __builtin_nanf("");
+    for (int i = lane; i < GB * D; i += kWave) outp[i] = (T)fill;
+    return;
+  }
+  const int nb = seq_blocks(L, cap);
+  const int64_t U = total * HH;
+  const int64_t us = before * HH + (int64_t)k * nb;
+  const int64_t ue = us + nb - 1;
+  const int wf = wave_of(us, W, U), wl = wave_of(ue, W, U);
+  if (wf == wl) return;  // finished inside one wave
+
+  float M[GB], lam[GB], o[GB][PER];
+#pragma unroll
+  for (int h = 0; h < GB; ++h) {
+    M[h] = -__builtin_inff();
+    lam[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[h][e] = 0.0f;
+  }
+  for (int c0 = wf; c0 <= wl; c0 += kWave) {
+    // pass 1: which candidates own a piece of the stream, and their (m, l)
+    const int c = c0 + lane;
+    const int64_t rb = range_begin(c, W, U);
+    const bool owner = c <= wl && rb < range_begin(c + 1, W, U);  // non-empty range inside [wf, wl]
+    const int64_t slot = (int64_t)c * 2 + ((c == wf && rb < us) ? 1 : 0);
+    float mc[GB], lc[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      mc[h] = owner ? a.part_ml[(slot * GB + h) * 2] : -__builtin_inff();
+      lc[h] = owner ? a.part_ml[(slot * GB + h) * 2 + 1] : 0.0f;
+    }
+    float f[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      const float Mn = fmaxf(M[h], wave_max(mc[h]));
+      const float rescale = fast_exp2(M[h] - Mn);  // earlier chunks of owners
+      f[h] = owner ? fast_exp2(mc[h] - Mn) : 0.0f;
+      lam[h] = lam[h] * rescale + wave_sum(f[h] * lc[h]);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[h][e] *= rescale;
+      M[h] = Mn;
+    }
+    // pass 2: weighted sum of the owners' outputs (loads of four owners in flight)
+    const uint64_t owners = __builtin_amdgcn_ballot_w64(owner);
+    const int n = 64 - __builtin_clzll(owners | 1ull);
+#pragma unroll 4
+    for (int j = 0; j < n; ++j) {
+      if (!((owners >> j) & 1ull)) continue;
+      const int64_t sj = __builtin_amdgcn_readlane((int)(slot & 0x7fffffff), j);
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f[h]), j));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[h][e] = fmaf(fj, a.part_o[(sj * GB + h) * D + lane + e * kWave], o[h][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GB; ++h) {
+    const float inv = 1.0f / lam[h];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) outp[h * D + lane + e * kWave] = (T)(o[h][e] * inv);
+  }
+}
+
 // Lanes per token: fewer lanes per token means fewer DPP reduction steps and
 // less redundant softmax work per block, at the price of more accumulator
 // registers per lane (head_dim / LPT floats per head).  8 for up to four heads
@@ -492,6 +746,17 @@ template <typename T, int D, int GB>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   constexpr int LPT = lanes_per_token<T, D, GB>();
   constexpr int NS = pipeline_stages<T, D, GB>();
+  if (a.balanced_waves > 0) {
+    const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
+    const int64_t merges = (int64_t)a.num_seqs * a.num_kv_heads * hsubs;
+    if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_balanced_kernel<T, D, GB, LPT, NS>), dim3(a.balanced_waves), dim3(64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_balanced_merge_kernel<T, D, GB>), dim3((unsigned)merges), dim3(64), 0, stream, a,
+                       a.balanced_waves);
+    return hipGetLastError();
+  }
   const int64_t rows = (int64_t)a.num_seqs * a.rows_per_seq;
   const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
   const int64_t items = rows * a.num_kv_heads * hsubs * a.max_parts;

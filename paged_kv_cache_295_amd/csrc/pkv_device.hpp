@@ -127,6 +127,54 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Exchange across lane groups for an all-reduce: the value of lane l ^ MASK
+// combined with the lane's own, for MASK in {8, 16, 32}.  8 is a DPP rotate by
+// 8 inside each row of 16 lanes; 16 and 32 use the permlane16/32 swaps, which
+// leave lane l's and lane (l ^ MASK)'s values in the two results.
+template <int MASK>
+__device__ __forceinline__ float xor_add(float x) {
+  static_assert(MASK == 8 || MASK == 16 || MASK == 32, "xor_add: mask 8, 16 or 32");
+  if constexpr (MASK == 8) {
+    return x + dpp_f32<0x128>(x);  // row_ror:8
+  } else {
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto r = MASK == 16 ? __builtin_amdgcn_permlane16_swap(b, b, false, false)
+                              : __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  }
+}
+
+template <int MASK>
+__device__ __forceinline__ float xor_max(float x) {
+  static_assert(MASK == 8 || MASK == 16 || MASK == 32, "xor_max: mask 8, 16 or 32");
+  if constexpr (MASK == 8) {
+    return fmaxf(x, dpp_f32<0x128>(x));
+  } else {
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto r = MASK == 16 ? __builtin_amdgcn_permlane16_swap(b, b, false, false)
+                              : __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  }
+}
+
+// All-reduce over the lanes that differ only in the bits >= log2(FROM) of the
+// lane id (the 64 / FROM lane groups of FROM consecutive lanes).
+template <int FROM>
+__device__ __forceinline__ float groups_add(float x) {
+  if constexpr (FROM <= 8) x = xor_add<8>(x);
+  if constexpr (FROM <= 16) x = xor_add<16>(x);
+  if constexpr (FROM <= 32) x = xor_add<32>(x);
+  return x;
+}
+
+template <int FROM>
+__device__ __forceinline__ float groups_max(float x) {
+  if constexpr (FROM <= 8) x = xor_max<8>(x);
+  if constexpr (FROM <= 16) x = xor_max<16>(x);
+  if constexpr (FROM <= 32) x = xor_max<32>(x);
+  return x;
+}
+
 __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
   const int lane = __lane_id();
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));

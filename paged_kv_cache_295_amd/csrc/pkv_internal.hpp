@@ -46,6 +46,9 @@ struct DecodeArgs {
   int32_t partition_tokens;
   int32_t max_parts;  // partitions the grid covers per query row
   float scale_log2;   // softmax scale * log2(e)
+  // > 0: balanced split over this many waves (decode only); part_o / part_ml
+  // then hold [waves][2][heads per wave][D] and [waves][2][heads per wave][2]
+  int32_t balanced_waves;
 };
 
 struct PrefillArgs {
@@ -70,6 +73,13 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 // Returns hipErrorInvalidValue if no instantiation covers the shape.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+
+// Waves of the balanced decode split: about four per compute unit, enough to
+// keep the MI355X's HBM busy while every wave reads a long run of blocks.
+#ifndef PKV_BALANCED_WAVES
+#define PKV_BALANCED_WAVES 1024
+#endif
+constexpr int kBalancedWaves = PKV_BALANCED_WAVES;
 
 // Heads processed together by one wave for a GQA group of size g.
 inline int heads_per_wave(int g) {

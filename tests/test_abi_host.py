@@ -85,24 +85,29 @@ def test_decode_validation(lib):
     assert decode(lib, d, maxlen=65) == SHAPE  # more than 16 * max_blocks
     assert decode(lib, d, part=17) == SHAPE
     assert decode(lib, d, scale=float("nan")) == SHAPE
-    # needs partitions -> a workspace
+    # fixed partitions -> a workspace
     assert decode(lib, d, maxb=256, maxlen=4096, part=256) == WS
     need = lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 4096, 256)
     assert need == 2 * 32 * 16 * (128 + 2) * 4
     assert decode(lib, d, maxb=256, maxlen=4096, part=256, ws=FAKE, wsb=need - 1) == WS
+    # balanced split -> its own workspace
+    assert decode(lib, d, maxb=256, maxlen=4096, part=0) == WS
+    need0 = lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 4096, 0)
+    assert decode(lib, d, maxb=256, maxlen=4096, part=0, ws=FAKE, wsb=need0 - 1) == WS
+    assert decode(lib, d, maxb=1 << 27, maxlen=64) == SHAPE
 
 
-def test_workspace_and_partition_choice(lib):
-    # one partition covers everything -> no workspace
+def test_workspace_sizes(lib):
+    W = lib.paged_attn_decode_split_waves()
+    assert W >= 256
+    # balanced split: [waves][2 slots][heads per wave][D + 2] floats, independent of the contexts
+    for (hq, hkv, gb) in [(32, 8, 4), (64, 8, 8), (8, 8, 1), (24, 4, 2), (12, 4, 1), (128, 8, 8)]:
+        for L in (1, 4096, 131072):
+            assert lib.paged_attn_decode_workspace_bytes(3, hq, hkv, 128, L, 0) == W * 2 * gb * 130 * 4
+    # fixed partitions: one partial per (row, head, partition); none if one partition covers everything
     assert lib.paged_attn_decode_workspace_bytes(4, 8, 8, 64, 200, 256) == 0
-    for (B, hq, hkv, L) in [(64, 32, 8, 4096), (8, 64, 8, 131072), (256, 32, 8, 2560), (4, 8, 8, 200)]:
-        p = lib.paged_attn_decode_partition_tokens(B, hq, hkv, L)
-        assert p >= 256 and p % 16 == 0 and (p & (p - 1)) == 0
-        ws = lib.paged_attn_decode_workspace_bytes(B, hq, hkv, 128, L, 0)
-        parts = -(-L // p)
-        assert ws == (0 if parts <= 1 else B * hq * parts * 130 * 4)
-    # long contexts with a small batch get 2048-token partitions
-    assert lib.paged_attn_decode_partition_tokens(8, 64, 8, 131072) == 2048
+    assert lib.paged_attn_decode_workspace_bytes(8, 64, 8, 128, 131072, 2048) == 8 * 64 * 64 * 130 * 4
+    assert lib.paged_attn_decode_workspace_bytes(2, 12, 8, 128, 100, 0) == 0  # Hq % Hkv != 0
 
 
 def prefill(lib, d, q=FAKE, nc=2, cmax=512, hq=32, maxb=256, scale=0.1):

@@ -282,3 +282,55 @@ def test_prefill_last_row_equals_decode():
     t.cuda.synchronize()
     # different kernels (MFMA with bf16 P vs. vector path): both within tolerance of each other
     assert oracle.max_abs_err(values(out)[0], pf) <= BF16_ABS
+
+
+# ------------------------------------------------------------------ balanced split
+
+BALANCED_CASES = [
+    ("tiny-many", [1, 2, 15, 16, 17] * 30),                      # 150 sequences: several scan chunks
+    ("zeros-between", [0, 33, 0, 0, 700, 0, 1, 0]),
+    ("one-giant", [20000] + [17] * 70),                          # one stream spans many wave ranges
+    ("ragged", list(range(1, 4000, 97))),
+]
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES, ids=lambda c: c[0])
+@pytest.mark.parametrize("heads", [(32, 8), (64, 8), (12, 4), (128, 8)], ids=lambda h: f"{h[0]}q{h[1]}kv")
+def test_balanced_split_parity(case, heads):
+    name, lens = case
+    hq, hkv = heads
+    w = small("bf16", hq, hkv, 128, lens, seed=13)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
+    got = values(run_decode(dw, partition_tokens=0))
+    check_attn(got, ref, "bf16", f"balanced {name} {heads}")
+
+
+def test_balanced_split_f32():
+    w = small("f32", 16, 4, 64, [3, 1000, 64, 65, 2500, 1], seed=14)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
+    check_attn(values(run_decode(dw, partition_tokens=0)), ref, "f32", "balanced f32")
+
+
+@pytest.mark.parametrize("part", [0, 512])
+def test_contract_violations_give_nan_not_faults(part):
+    """Context longer than the table, negative context, block id out of range:
+    the kernels bounds-check them and answer NaN for the sequences concerned;
+    the other sequences are unaffected."""
+    w = small("bf16", 32, 8, 128, [100, 300, 50, 2000], seed=15, max_blocks=128)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
+    lens = w.context_lens.copy()
+    lens[0] = 128 * 16 + 5   # longer than the table
+    lens[2] = -7             # negative
+    tables = w.block_tables.copy()
+    tables[1, 3] = w.num_blocks + 1000  # out of the pool
+    dw.lens = to_dev(lens.astype(np.int32), "bf16")
+    dw.tables = to_dev(tables, "bf16")
+    got = values(run_decode(dw, partition_tokens=part, max_context_len=128 * 16))
+    assert np.isnan(got[0]).all() and np.isnan(got[1]).all() and np.isnan(got[2]).all()
+    check_attn(got[3:], ref[3:], "bf16", "unaffected sequence")
