@@ -160,7 +160,7 @@ def main():
                    "block_size": 16, "num_blocks": w.num_blocks, "context_tokens": int(w.context_lens.sum()),
                    "max_context_len": w.max_context_len,
                    "split": f"fixed partitions of {part} tokens" if part else
-                            f"balanced over {pkv.decode_split_waves()} wavefronts",
+                            f"balanced over {pkv.decode_split_waves(w.num_q_heads, w.num_kv_heads)} wavefronts",
                    "kv_bytes_per_step": kv_bytes, "llc": "cold (512 MB overwrite per step)" if args.cold else "warm",
                    "layers_per_step": 1},
         "seq_tokens_per_s": round(seq_tok_s, 1),

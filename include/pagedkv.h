@@ -98,18 +98,21 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
  * in exact arithmetic.  Two ways of cutting:
  *
  *   partition_tokens == 0 (recommended): balanced split.  The whole batch's
- *     work -- every (sequence, kv head, 16-token block) -- is divided into
- *     paged_attn_decode_split_waves() equal runs of consecutive blocks, one
- *     per wavefront, so every wavefront reads the same amount of K/V whatever
- *     the mix of context lengths; a context is cut wherever a run ends.  The
- *     workspace size does not depend on the context lengths.
+ *     work -- every (sequence, kv head, 16-token block) -- is divided over
+ *     paged_attn_decode_split_waves(num_q_heads, num_kv_heads) wavefronts in
+ *     runs of consecutive blocks.  Each (sequence, kv head) stream is charged
+ *     its blocks plus a fixed cost for starting it, and every wavefront gets
+ *     the same total charge, so all finish together whatever the mix of
+ *     context lengths; a context is cut wherever a run ends.  The workspace
+ *     size does not depend on the context lengths.
  *   partition_tokens > 0 (a multiple of 16): fixed partitions of that many
  *     tokens per sequence, one wavefront each.
  *
+ * paged_attn_decode_split_waves returns 0 for invalid head counts.
  * paged_attn_decode_workspace_bytes returns the workspace paged_attn_decode
  * needs for these sizes (0 if none).
  */
-int32_t paged_attn_decode_split_waves(void);
+int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads);
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_context_len, int32_t partition_tokens);
 

@@ -56,7 +56,7 @@ def load_library():
     cdp = ctypes.POINTER(CacheDesc)
     lib.paged_kv_write.argtypes = [vp, vp, vp, i64, vp, vp, cdp, vp]
     lib.paged_kv_write.restype = ctypes.c_int
-    lib.paged_attn_decode_split_waves.argtypes = []
+    lib.paged_attn_decode_split_waves.argtypes = [i32, i32]
     lib.paged_attn_decode_split_waves.restype = i32
     lib.paged_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_attn_decode_workspace_bytes.restype = sz
@@ -138,9 +138,9 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
     _check(st, "paged_kv_write")
 
 
-def decode_split_waves() -> int:
+def decode_split_waves(num_q_heads: int, num_kv_heads: int) -> int:
     """Wavefronts the balanced decode split (partition_tokens=0) divides a batch's work over."""
-    return int(load_library().paged_attn_decode_split_waves())
+    return int(load_library().paged_attn_decode_split_waves(num_q_heads, num_kv_heads))
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

@@ -25,11 +25,11 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
-// Balanced split (partition_tokens == 0): kBalancedWaves waves, each with up
-// to two partials of heads_per_wave heads.
+// Balanced split (partition_tokens == 0): balanced_waves(gb) waves, each with
+// up to two partials of gb = heads_per_wave heads.
 size_t balanced_workspace(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
   const int gb = heads_per_wave(num_q_heads / num_kv_heads);
-  return (size_t)kBalancedWaves * 2 * gb * ((size_t)head_dim + 2) * sizeof(float);
+  return (size_t)balanced_waves(gb) * 2 * gb * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 // Fixed partitions of `part` tokens: one partial per (row, head, partition).
@@ -70,7 +70,10 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
   return from_hip(launch_kv_write(a, as_stream(hip_stream)));
 }
 
-int32_t paged_attn_decode_split_waves(void) { return kBalancedWaves; }
+int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  return balanced_waves(heads_per_wave(num_q_heads / num_kv_heads));
+}
 
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
@@ -125,7 +128,7 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
   a.partition_tokens = part;
   a.max_parts = (int32_t)max_parts64;
   a.scale_log2 = scale * kLog2eHost;
-  a.balanced_waves = balanced ? kBalancedWaves : 0;
+  a.balanced_waves = balanced ? balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads)) : 0;
   return from_hip(launch_decode(a, as_stream(hip_stream)));
 }
 

@@ -489,19 +489,32 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
 
 // ---------------------------------------------------------------- balanced split
 //
-// The work of a decode step is the list of units (sequence s, stream k, block
-// j), streams k = (kv head, head subgroup) of a sequence, ordered by s, then k,
-// then j.  With U units and W waves, wave w takes units [w U / W, (w+1) U / W):
-// every wave reads the same number of K/V blocks (within one) whatever the mix
-// of context lengths, so no compute unit idles behind a long sequence.  A
-// stream wholly inside one wave's range is finished there; a stream cut by a
-// range boundary leaves (m, l, o) partials -- a wave has at most two: its first
-// segment (slot 0) and its last (slot 1) -- which the merge kernel combines.
+// The work of a decode step is the list of streams (sequence s, stream k),
+// k = (kv head, head subgroup), ordered by s then k.  A stream of nb blocks
+// costs nb + kSegCost: one unit per K/V block plus a fixed charge, in block
+// units, for what every segment pays once (reading q, filling the load
+// pipeline, combining the token groups and storing).  With total cost C and W
+// waves, wave w takes the cost interval [w C / W, (w+1) C / W); the first
+// kSegCost units of a stream stand for its fixed charge and the next nb units
+// are its blocks, so a wave that starts several short streams reads fewer
+// blocks and every wave finishes at about the same time whatever the mix of
+// context lengths.  A stream whose blocks lie wholly inside one wave's
+// interval is finished there; a stream cut by an interval boundary leaves
+// (m, l, o) partials -- a wave has at most two: its first segment (slot 0) and
+// its last (slot 1) -- which the merge kernel combines.
 //
-// Sequences with a context outside [0, 16 * max_blocks] contribute no units;
+// Sequences with a context outside [0, 16 * max_blocks] contribute no cost;
 // the merge kernel writes NaN for them (and 0 for an empty context).
 
+#ifndef PKV_SEGMENT_COST
+#define PKV_SEGMENT_COST 8
+#endif
+constexpr int kSegCost = PKV_SEGMENT_COST;
+
 __device__ __forceinline__ int seq_blocks(int L, int cap) { return (L >= 0 && L <= cap) ? (L + kBlock - 1) / kBlock : 0; }
+
+// Cost of all HH streams of a sequence with nb blocks.
+__device__ __forceinline__ int64_t seq_cost(int nb, int HH) { return nb > 0 ? (int64_t)HH * (nb + kSegCost) : 0; }
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -509,57 +522,55 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// x + (x of the lane that DPP control kCtrl names), 0 where it names none.
 template <int kCtrl, int kRowMask = 0xF>
-__device__ __forceinline__ int dpp_i32(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, kCtrl, kRowMask, 0xF, false);
+__device__ __forceinline__ int64_t dpp_add_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)x, kCtrl, kRowMask, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)((uint64_t)x >> 32), kCtrl, kRowMask, 0xF, false);
+  return x + (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Inclusive prefix sum over the 64 lanes (DPP: row_shr within rows of 16,
 // then row_bcast:15 / row_bcast:31 across rows).
-__device__ __forceinline__ int wave_incl_scan_int(int x) {
-  x += dpp_i32<0x111>(x);         // row_shr:1
-  x += dpp_i32<0x112>(x);         // row_shr:2
-  x += dpp_i32<0x114>(x);         // row_shr:4
-  x += dpp_i32<0x118>(x);         // row_shr:8
-  x += dpp_i32<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
-  x += dpp_i32<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x) {
+  x = dpp_add_i64<0x111>(x);         // row_shr:1
+  x = dpp_add_i64<0x112>(x);         // row_shr:2
+  x = dpp_add_i64<0x114>(x);         // row_shr:4
+  x = dpp_add_i64<0x118>(x);         // row_shr:8
+  x = dpp_add_i64<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
+  x = dpp_add_i64<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
   return x;
 }
 
-__device__ __forceinline__ int wave_sum_int(int x) {
-  return __builtin_amdgcn_readlane(wave_incl_scan_int(x), kWave - 1);
-}
-
-// Total blocks over all sequences, and the blocks of the sequences before s
+// Total cost over all sequences, and the cost of the sequences before s
 // (every lane gets both); one pass over the lengths.
-__device__ __forceinline__ void block_counts(const int32_t* __restrict__ lens, int B, int s, int cap, int64_t& total,
-                                             int64_t& before) {
+__device__ __forceinline__ void cost_counts(const int32_t* __restrict__ lens, int B, int s, int cap, int HH,
+                                            int64_t& total, int64_t& before) {
   total = 0;
   before = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int i = c0 + __lane_id();
-    const int nb = i < B ? seq_blocks(lens[i], cap) : 0;
-    const int incl = wave_incl_scan_int(nb);
-    total += __builtin_amdgcn_readlane(incl, kWave - 1);
+    const int64_t incl = wave_incl_scan(i < B ? seq_cost(seq_blocks(lens[i], cap), HH) : 0);
+    const int64_t all = readlane64(incl, kWave - 1);
+    total += all;
     if (s >= c0 + kWave) {
-      before += __builtin_amdgcn_readlane(incl, kWave - 1);
+      before += all;
     } else if (s > c0) {
-      before += __builtin_amdgcn_readlane(incl, s - c0 - 1);
+      before += readlane64(incl, s - c0 - 1);
     }
   }
   total = uniform64(total);
   before = uniform64(before);
 }
 
-// Total blocks over all sequences (every lane gets it).
-__device__ __forceinline__ int64_t total_blocks(const int32_t* __restrict__ lens, int B, int cap) {
-  int64_t tot = 0, before = 0;
-  block_counts(lens, B, 0, cap, tot, before);
-  return tot;
-}
-
 __device__ __forceinline__ int64_t range_begin(int w, int W, int64_t U) { return (int64_t)w * U / W; }
-// The wave whose range holds unit u.
+// The wave whose range holds cost unit u.
 __device__ __forceinline__ int wave_of(int64_t u, int W, int64_t U) { return (int)(((u + 1) * W + U - 1) / U) - 1; }
 
 template <typename T, int D, int GB, int LPT, int NS>
@@ -574,25 +585,26 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a)
   const int cap = a.max_blocks_per_seq * kBlock;
   const int32_t* __restrict__ lens = a.context_lens;
 
-  const int64_t U = total_blocks(lens, B, cap) * HH;
+  int64_t U, unused;
+  cost_counts(lens, B, 0, cap, HH, U, unused);
   const int64_t u0 = range_begin(w, W, U), u1 = range_begin(w + 1, W, U);
   if (u0 >= u1) return;
 
-  // locate u0: the sequence s whose units [HH cum, HH (cum + nb)) hold it
+  // locate u0: the sequence s whose cost interval [cum, cum + cost) holds it
   int s = 0;
   int64_t cum = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int i = c0 + lane;
-    const int nb = i < B ? seq_blocks(lens[i], cap) : 0;
-    const int incl = wave_incl_scan_int(nb);
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && (cum + incl) * HH > u0);
+    const int64_t c = i < B ? seq_cost(seq_blocks(lens[i], cap), HH) : 0;
+    const int64_t incl = wave_incl_scan(c);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && cum + incl > u0);
     if (hit) {
       const int ln = __builtin_ctzll(hit);
       s = c0 + ln;
-      cum += __builtin_amdgcn_readlane(incl - nb, ln);
+      cum += readlane64(incl - c, ln);
       break;
     }
-    cum += __builtin_amdgcn_readlane(incl, kWave - 1);
+    cum += readlane64(incl, kWave - 1);
   }
   s = __builtin_amdgcn_readfirstlane(s);
   cum = uniform64(cum);
@@ -600,12 +612,16 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a)
   Segment<T, D, GB, LPT, NS> seg;
   int L = __builtin_amdgcn_readfirstlane(lens[s]);
   int nb = seq_blocks(L, cap);
+  bool first = true;
   for (int64_t u = u0;;) {
-    const int r = (int)(u - cum * HH);  // unit offset inside sequence s
-    const int k = r / nb, j = r - k * nb;
+    const int64_t span = nb + kSegCost;  // cost of one stream of sequence s
+    const int k = (int)((u - cum) / span);
+    const int64_t sb = cum + (int64_t)k * span + kSegCost;  // the stream's first block
+    const int64_t ub = u > sb ? u : sb;
+    if (ub >= u1) break;  // the rest of the range is the stream's fixed charge
+    const int64_t seg_end = min(u1, sb + nb);
+    const int j = (int)(ub - sb), jn = (int)(seg_end - sb);
     const int g = k / hsubs, hs = k - g * hsubs;
-    const int64_t seg_end = min(u1, cum * HH + (int64_t)(k + 1) * nb);
-    const int jn = j + (int)(seg_end - u);
     const int h0 = g * G + hs * GB;
     const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)s * a.num_q_heads + h0) * D;
     seg.run(a, qrow, a.block_tables + (int64_t)s * a.max_blocks_per_seq + j, g, j, jn - j, min(L, jn * kBlock));
@@ -613,13 +629,14 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a)
     if (j == 0 && jn == nb) {
       seg.store_out(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D);
     } else {
-      const int64_t slot = (int64_t)w * 2 + (u == u0 ? 0 : 1);
+      const int64_t slot = (int64_t)w * 2 + (first ? 0 : 1);
       seg.store_partial(a.part_o + slot * GB * D, D, a.part_ml + slot * GB * 2, 2);
     }
+    first = false;
     u = seg_end;
     if (u >= u1) break;
     if (k + 1 == HH) {  // next sequence that has blocks (one exists: u < U)
-      cum += nb;
+      cum += (int64_t)HH * span;
       do {
         ++s;
         L = __builtin_amdgcn_readfirstlane(lens[s]);
@@ -652,16 +669,16 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
   T* outp = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D;
 
   const int L = a.context_lens[s];
-  int64_t total, before;
-  block_counts(a.context_lens, B, s, cap, total, before);
   if (L < 0 || L > cap || L == 0) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
     for (int i = lane; i < GB * D; i += kWave) outp[i] = (T)fill;
     return;
   }
+  int64_t U, before;
+  cost_counts(a.context_lens, B, s, cap, HH, U, before);
   const int nb = seq_blocks(L, cap);
-  const int64_t U = total * HH;
-  const int64_t us = before * HH + (int64_t)k * nb;
+  const int64_t as = before + (int64_t)k * (nb + kSegCost);  // the stream's cost interval starts here
+  const int64_t us = as + kSegCost;                           // and its blocks here
   const int64_t ue = us + nb - 1;
   const int wf = wave_of(us, W, U), wl = wave_of(ue, W, U);
   if (wf == wl) return;  // finished inside one wave
@@ -679,7 +696,8 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
     const int c = c0 + lane;
     const int64_t rb = range_begin(c, W, U);
     const bool owner = c <= wl && rb < range_begin(c + 1, W, U);  // non-empty range inside [wf, wl]
-    const int64_t slot = (int64_t)c * 2 + ((c == wf && rb < us) ? 1 : 0);
+    // slot 1 if wave c worked on an earlier stream first, i.e. its range starts before this stream's
+    const int64_t slot = (int64_t)c * 2 + ((c == wf && rb < as) ? 1 : 0);
     float mc[GB], lc[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {

@@ -74,19 +74,24 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
-// Waves of the balanced decode split: about four per compute unit, enough to
-// keep the MI355X's HBM busy while every wave reads a long run of blocks.
-#ifndef PKV_BALANCED_WAVES
-#define PKV_BALANCED_WAVES 1024
-#endif
-constexpr int kBalancedWaves = PKV_BALANCED_WAVES;
-
 // Heads processed together by one wave for a GQA group of size g.
 inline int heads_per_wave(int g) {
   if (g % 8 == 0) return 8;
   if (g % 4 == 0) return 4;
   if (g % 2 == 0) return 2;
   return 1;
+}
+
+// Waves of the balanced decode split, by heads per wave.  One wave per SIMD
+// (1024 on the MI355X's 256 compute units) keeps HBM busy when a wave's
+// vector work per block is small; eight heads per wave double that work, and
+// a second wave per SIMD hides its latency.
+#ifndef PKV_BALANCED_WAVES
+#define PKV_BALANCED_WAVES 0
+#endif
+inline int balanced_waves(int gb) {
+  if (PKV_BALANCED_WAVES > 0) return PKV_BALANCED_WAVES;
+  return gb >= 8 ? 2048 : 1024;
 }
 
 }  // namespace pkv

@@ -98,12 +98,14 @@ def test_decode_validation(lib):
 
 
 def test_workspace_sizes(lib):
-    W = lib.paged_attn_decode_split_waves()
-    assert W >= 256
     # balanced split: [waves][2 slots][heads per wave][D + 2] floats, independent of the contexts
     for (hq, hkv, gb) in [(32, 8, 4), (64, 8, 8), (8, 8, 1), (24, 4, 2), (12, 4, 1), (128, 8, 8)]:
+        W = lib.paged_attn_decode_split_waves(hq, hkv)
+        assert W >= 256
         for L in (1, 4096, 131072):
             assert lib.paged_attn_decode_workspace_bytes(3, hq, hkv, 128, L, 0) == W * 2 * gb * 130 * 4
+    assert lib.paged_attn_decode_split_waves(12, 8) == 0
+    assert lib.paged_attn_decode_split_waves(0, 8) == 0
     # fixed partitions: one partial per (row, head, partition); none if one partition covers everything
     assert lib.paged_attn_decode_workspace_bytes(4, 8, 8, 64, 200, 256) == 0
     assert lib.paged_attn_decode_workspace_bytes(8, 64, 8, 128, 131072, 2048) == 8 * 64 * 64 * 130 * 4
