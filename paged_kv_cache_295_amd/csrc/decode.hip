@@ -178,22 +178,32 @@ struct Segment {
   float m[GB], l[GB], acc[GB][CPL][EPC];
   bool bad_block;
   int tg, li;
+  int lane_base;  // byte offset of this lane's first chunk inside a tile
+  const char* __restrict__ kc;
+  const char* __restrict__ vc;
+  float sl2;
 
-  __device__ __forceinline__ Segment() {
+  static constexpr int64_t kTileBytes = (int64_t)kBlock * D * sizeof(T);
+
+  __device__ __forceinline__ explicit Segment(const DecodeArgs& a) {
     const int lane = __lane_id();
     tg = lane / LPT;
     li = lane % LPT;
+    lane_base = tg * (D * (int)sizeof(T)) + li * 16;
+    kc = reinterpret_cast<const char*>(a.k_cache);
+    vc = reinterpret_cast<const char*>(a.v_cache);
+    sl2 = a.scale_log2;
   }
 
-  // Attend the GB query rows at qrow (head h0 of the row) over tokens
-  // [16 * blk0, end) of one sequence, whose blocks blk0 .. blk0 + nblk - 1 are
-  // listed at table[0 .. nblk - 1], for kv head g.
-  __device__ __forceinline__ void run(const DecodeArgs& a, const T* __restrict__ qrow,
-                                      const int32_t* __restrict__ table, int g, int blk0, int nblk, int end) {
+  // The chunks of the GB query rows at qrow (head h0 of the row) this lane multiplies.
+  __device__ __forceinline__ void load_q(const T* __restrict__ qrow) {
 #pragma unroll
     for (int h = 0; h < GB; ++h)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) qv[h][c] = load_chunk(qrow + h * D + (c * LPT + li) * EPC);
+  }
+
+  __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
       m[h] = kMaxInit;
@@ -204,109 +214,114 @@ struct Segment {
         for (int e = 0; e < EPC; ++e) acc[h][c][e] = 0.0f;
     }
     bad_block = false;
+  }
 
-    const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache);
-    const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache);
-    const int64_t tile_bytes = (int64_t)kBlock * D * sizeof(T);
-    const int64_t blk_stride = tile_bytes * a.num_kv_heads;
+  // One K tile and one V tile (16 tokens of one kv head) at byte offset off of
+  // the caches.  Every tile is loaded whole (rows past the context in a last
+  // block are still inside it): one constant per-lane offset plus immediates,
+  // so no address arithmetic sits between the loads of consecutive tiles.
+  __device__ __forceinline__ void load_tile(Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], int64_t off) const {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int o = lane_base + p * TPP * (D * (int)sizeof(T)) + c * LPT * 16;
+        if constexpr (kStreamKV) {
+          kk[p][c] = load_chunk_stream(kc + off + o);
+          vv[p][c] = load_chunk_stream(vc + off + o);
+        } else {
+          kk[p][c] = load_chunk(kc + off + o);
+          vv[p][c] = load_chunk(vc + off + o);
+        }
+      }
+  }
+
+  // Attend the query rows over one tile whose first token (of this lane's
+  // pass 0) is tok0; tokens at or past `end` are masked.
+  __device__ __forceinline__ void compute(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL], int tok0, int end) {
+    float x[NP * GB];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) d = E::dot(qv[h][c], kk[p][c], d);
+        x[p * GB + h] = d;
+      }
+    group_sum_all<LPT>(x);
+    float sc[NP][GB];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? x[p * GB + h] * sl2 : -__builtin_inff();
+    bool need = false;
+    float bm[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      bm[h] = sc[0][h];
+#pragma unroll
+      for (int p = 1; p < NP; ++p) bm[h] = fmaxf(bm[h], sc[p][h]);
+      need |= bm[h] > m[h] + kRescaleSlack;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const float mn = fmaxf(m[h], bm[h]);
+        const float alpha = fast_exp2(m[h] - mn);
+        m[h] = mn;
+        l[h] *= alpha;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[h][c][e] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      float ls = l[h];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const float pr = fast_exp2(sc[p][h] - m[h]);
+        sc[p][h] = pr;
+        ls += pr;
+      }
+      l[h] = ls;
+    }
+    // Rows past `end` may hold NaN: a zero weight is not enough (0 * NaN), so
+    // their V words are replaced by 0.  Selects on every block keep a single
+    // code path.
+    Chunk vz[NP][CPL];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const bool ok = tok0 + p * TPP < end;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vz[p][c].w[w] = ok ? vv[p][c].w[w] : 0u;
+    }
+    PV<T, NP, CPL, GB>::apply(sc, vz, acc);
+  }
+
+  // Attend the GB query rows at qrow (head h0 of the row) over tokens
+  // [16 * blk0, end) of one sequence, whose blocks blk0 .. blk0 + nblk - 1 are
+  // listed at table[0 .. nblk - 1], for kv head g.
+  __device__ __forceinline__ void run(const DecodeArgs& a, const T* __restrict__ qrow,
+                                      const int32_t* __restrict__ table, int g, int blk0, int nblk, int end) {
+    load_q(qrow);
+    reset();
+    const int64_t blk_stride = kTileBytes * a.num_kv_heads;
     const int num_blocks = a.num_blocks;
-    // byte offset of this lane's chunk (pass p, chunk c) inside a tile
-    const int lane_base = tg * (D * (int)sizeof(T)) + li * 16;
-
-    auto block_off = [&](int jb) -> int64_t {
-      int p = table[jb];  // uniform: a scalar load
+    // Table entries are uniform: scalar loads (the table is a read-only,
+    // non-aliased argument), counted apart from the vector K/V loads.
+    auto tile_off = [&](int p) -> int64_t {
       if (p < 0 || p >= num_blocks) {
         bad_block = true;
         p = 0;
       }
-      return (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
+      return (int64_t)p * blk_stride + (int64_t)g * kTileBytes;
     };
-
-    // Every block is loaded whole (rows past `end` in the last block are still
-    // inside that block): one constant per-lane offset plus immediates, so no
-    // address arithmetic sits between the loads of consecutive blocks.
-    auto load = [&](Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], int64_t off) {
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int o = lane_base + p * TPP * (D * (int)sizeof(T)) + c * LPT * 16;
-          if constexpr (kStreamKV) {
-            kk[p][c] = load_chunk_stream(kc + off + o);
-            vv[p][c] = load_chunk_stream(vc + off + o);
-          } else {
-            kk[p][c] = load_chunk(kc + off + o);
-            vv[p][c] = load_chunk(vc + off + o);
-          }
-        }
-    };
-
-    const float sl2 = a.scale_log2;
-    auto compute = [&](const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL], int jb) {
-      float x[NP * GB];
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int h = 0; h < GB; ++h) {
-          float d = 0.0f;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) d = E::dot(qv[h][c], kk[p][c], d);
-          x[p * GB + h] = d;
-        }
-      group_sum_all<LPT>(x);
-      const int tok0 = (blk0 + jb) * kBlock + tg;  // this lane's token of pass 0
-      float sc[NP][GB];
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? x[p * GB + h] * sl2 : -__builtin_inff();
-      bool need = false;
-      float bm[GB];
-#pragma unroll
-      for (int h = 0; h < GB; ++h) {
-        bm[h] = sc[0][h];
-#pragma unroll
-        for (int p = 1; p < NP; ++p) bm[h] = fmaxf(bm[h], sc[p][h]);
-        need |= bm[h] > m[h] + kRescaleSlack;
-      }
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-#pragma unroll
-        for (int h = 0; h < GB; ++h) {
-          const float mn = fmaxf(m[h], bm[h]);
-          const float alpha = fast_exp2(m[h] - mn);
-          m[h] = mn;
-          l[h] *= alpha;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[h][c][e] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < GB; ++h) {
-        float ls = l[h];
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const float pr = fast_exp2(sc[p][h] - m[h]);
-          sc[p][h] = pr;
-          ls += pr;
-        }
-        l[h] = ls;
-      }
-      // Rows past `end` may hold NaN: a zero weight is not enough (0 * NaN), so
-      // their V words are replaced by 0.  Selects on every block keep a single
-      // code path.
-      Chunk vz[NP][CPL];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const bool ok = tok0 + p * TPP < end;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) vz[p][c].w[w] = ok ? vv[p][c].w[w] : 0u;
-      }
-      PV<T, NP, CPL, GB>::apply(sc, vz, acc);
-    };
+    auto block_off = [&](int jb) -> int64_t { return tile_off(table[jb]); };
 
     // NS register stages: while block jb is computed, blocks jb+1 .. jb+NS-1
     // are in flight and block jb+NS is issued right after.  The prologue fills
@@ -319,20 +334,23 @@ struct Segment {
     Chunk kS[NS][NP][CPL], vS[NS][NP][CPL];
     const int last = nblk - 1;
     int64_t offs[NS];
+    int first[2 * NS];  // the first 2 NS entries, fetched together
+#pragma unroll
+    for (int i = 0; i < 2 * NS; ++i) first[i] = table[min(i, last)];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      load(kS[st], vS[st], block_off(min(st, last)));
+      load_tile(kS[st], vS[st], tile_off(first[st]));
       // each stage's loads are issued before the next stage's: waits are in order
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int st = 0; st < NS; ++st) offs[st] = block_off(min(NS + st, last));
+    for (int st = 0; st < NS; ++st) offs[st] = tile_off(first[NS + st]);
     for (int jb = 0;; jb += NS) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        compute(kS[st], vS[st], jb + st);
+        compute(kS[st], vS[st], (blk0 + jb + st) * kBlock + tg, end);
         const int64_t next = block_off(min(jb + 2 * NS + st, last));
-        load(kS[st], vS[st], offs[st]);
+        load_tile(kS[st], vS[st], offs[st]);
         offs[st] = next;
       }
       if (jb + NS >= nblk) break;
@@ -405,7 +423,7 @@ struct Segment {
 // partition of P tokens).  Also serves float32 prefill rows (one partition
 // covering the whole table).
 template <typename T, int D, int GB, int LPT, int NS>
-__global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a, const int32_t* __restrict__ tables) {
   const int lane = __lane_id();
   const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
   int64_t t = blockIdx.x;
@@ -437,9 +455,9 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
   const int blk0 = start / kBlock;
   const int nblk = (end - start + kBlock - 1) / kBlock;
 
-  Segment<T, D, GB, LPT, NS> seg;
+  Segment<T, D, GB, LPT, NS> seg(a);
   const T* qrow = reinterpret_cast<const T*>(a.q) + (row * a.num_q_heads + h0) * (int64_t)D;
-  seg.run(a, qrow, a.block_tables + (int64_t)ri.seq * a.max_blocks_per_seq + blk0, g, blk0, nblk, end);
+  seg.run(a, qrow, tables + (int64_t)ri.seq * a.max_blocks_per_seq + blk0, g, blk0, nblk, end);
   seg.merge_groups();
   if (nparts == 1) {
     seg.store_out(outp);
@@ -574,7 +592,8 @@ __device__ __forceinline__ int64_t range_begin(int w, int W, int64_t U) { return
 __device__ __forceinline__ int wave_of(int64_t u, int W, int64_t U) { return (int)(((u + 1) * W + U - 1) / U) - 1; }
 
 template <typename T, int D, int GB, int LPT, int NS>
-__global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
+                                                              const int32_t* __restrict__ lens) {
   const int lane = __lane_id();
   const int W = gridDim.x;
   const int w = blockIdx.x;
@@ -583,7 +602,6 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a)
   const int hsubs = G / GB;
   const int HH = a.num_kv_heads * hsubs;  // streams per sequence
   const int cap = a.max_blocks_per_seq * kBlock;
-  const int32_t* __restrict__ lens = a.context_lens;
 
   int64_t U, unused;
   cost_counts(lens, B, 0, cap, HH, U, unused);
@@ -609,8 +627,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a)
   s = __builtin_amdgcn_readfirstlane(s);
   cum = uniform64(cum);
 
-  Segment<T, D, GB, LPT, NS> seg;
-  int L = __builtin_amdgcn_readfirstlane(lens[s]);
+  Segment<T, D, GB, LPT, NS> seg(a);
+  int L = lens[s];
   int nb = seq_blocks(L, cap);
   bool first = true;
   for (int64_t u = u0;;) {
@@ -624,7 +642,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a)
     const int g = k / hsubs, hs = k - g * hsubs;
     const int h0 = g * G + hs * GB;
     const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)s * a.num_q_heads + h0) * D;
-    seg.run(a, qrow, a.block_tables + (int64_t)s * a.max_blocks_per_seq + j, g, j, jn - j, min(L, jn * kBlock));
+    seg.run(a, qrow, tables + (int64_t)s * a.max_blocks_per_seq + j, g, j, jn - j, min(L, jn * kBlock));
     seg.merge_groups();
     if (j == 0 && jn == nb) {
       seg.store_out(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D);
@@ -639,7 +657,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a)
       cum += (int64_t)HH * span;
       do {
         ++s;
-        L = __builtin_amdgcn_readfirstlane(lens[s]);
+        L = lens[s];
         nb = seq_blocks(L, cap);
       } while (nb == 0);
     }
@@ -754,7 +772,7 @@ constexpr int lanes_per_token() {
   constexpr int want = GB >= 8 ? 16 : PKV_DECODE_LPT_SMALL_GROUP;
   return row_chunks < want ? row_chunks : want;
 }
-// Register stages of the K/V prefetch pipeline.
+// Register stages of the K/V prefetch pipeline (fixed partitions).
 template <typename T, int D, int GB>
 constexpr int pipeline_stages() {
   return PKV_DECODE_STAGES;
@@ -768,7 +786,8 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
     const int64_t merges = (int64_t)a.num_seqs * a.num_kv_heads * hsubs;
     if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_balanced_kernel<T, D, GB, LPT, NS>), dim3(a.balanced_waves), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_balanced_kernel<T, D, GB, LPT, NS>), dim3(a.balanced_waves), dim3(64), 0, stream, a,
+                       a.block_tables, a.context_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_balanced_merge_kernel<T, D, GB>), dim3((unsigned)merges), dim3(64), 0, stream, a,
@@ -780,7 +799,8 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t items = rows * a.num_kv_heads * hsubs * a.max_parts;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, GB, LPT, NS>), dim3((unsigned)items), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, GB, LPT, NS>), dim3((unsigned)items), dim3(64), 0, stream, a,
+                     a.block_tables);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   const int64_t merges = rows * a.num_q_heads;

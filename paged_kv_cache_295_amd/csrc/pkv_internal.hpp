@@ -75,7 +75,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
 // Heads processed together by one wave for a GQA group of size g.
-inline int heads_per_wave(int g) {
+constexpr int heads_per_wave(int g) {
   if (g % 8 == 0) return 8;
   if (g % 4 == 0) return 4;
   if (g % 2 == 0) return 2;
@@ -89,7 +89,7 @@ inline int heads_per_wave(int g) {
 #ifndef PKV_BALANCED_WAVES
 #define PKV_BALANCED_WAVES 0
 #endif
-inline int balanced_waves(int gb) {
+constexpr int balanced_waves(int gb) {
   if (PKV_BALANCED_WAVES > 0) return PKV_BALANCED_WAVES;
   return gb >= 8 ? 2048 : 1024;
 }
