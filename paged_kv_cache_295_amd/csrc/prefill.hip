@@ -10,24 +10,36 @@
 //
 // Design (one workgroup = 4 waves, 128 "M rows" = G query heads x 128/G chunk
 // rows sharing one kv head):
-//  * Key tiles of 64 tokens (4 cache blocks) are gathered through the block
-//    table into LDS once per workgroup and shared by the G heads of the group:
-//    K row-major [key][dim], V transposed [dim][key] (pairs of keys packed per
-//    dword on the way in), both padded so the MFMA operand reads are free of
-//    bank conflicts.  The next tile's global loads are in flight while the
-//    current one is computed.
+//  * Key tiles of 64 tokens (4 cache blocks, one per wave) stream through NS
+//    LDS stages with direct-to-LDS loads, NS - 1 tiles ahead of the compute;
+//    the block-table entry of a wave's block is a scalar load fetched a tile
+//    earlier.  K and V land row-major with their 16-byte chunks XOR-swizzled
+//    by row (chunk c of key row r at position c ^ (r mod chunks-per-row)), so
+//    the operand reads below hit distinct LDS banks.  Blocks past the keys
+//    any row may see load block 0, and once the last tile has landed its V
+//    rows past those keys are zeroed in LDS: masked keys then carry exact
+//    zeros, never the contents of unused cache slots (0 * NaN is NaN).
 //  * Transposed formulation so that each lane owns one query row:
 //      S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = K (LDS), B = Q (registers)
-//      O^T += V^T P^T   A = V^T (LDS), B = P (registers, from S^T's lanes)
+//      O^T += V^T P^T   A = V^T (LDS transpose reads), B = P (registers)
 //    In the 32x32 accumulator layout lane l holds column l % 32 (its query
 //    row) and 16 of the 32 rows, the other 16 sit in lane l ^ 32; so the row
 //    max needs one exchange with lane l ^ 32, and the softmax rescale of O^T
 //    is a per-lane multiply.  P feeds the second product straight from the
-//    registers of the first: the key order of the K dimension is permuted the
-//    same way in A (two 8-byte V^T reads) and B, which leaves the sum unchanged.
+//    registers of the first: its key order (keys 4h..4h+3 and 8+4h..8+4h+3 of
+//    each 16-key step for half h of the wave) is what two ds_read_b64_tr_b16
+//    per operand deliver from the row-major V tile: within each 16-lane group,
+//    lane i receives element i mod 4 of the 8-byte rows addressed by lanes
+//    i/4 + 4k, k = 0..3, so lanes addressing 4 consecutive keys x 4 dims hand
+//    every lane 4 consecutive keys of one dim.
+//  * LDS reads are issued from asm blocks (with their own wait): the compiler
+//    cannot tell which pending direct-to-LDS load a read depends on and would
+//    otherwise drain them all before every read.
 //  * Online softmax in the log2 domain; causal mask by select (never by
-//    multiplying, so NaN-filled unused slots cannot leak); P is rounded to bf16
-//    for the matrix cores, accumulation stays float32.
+//    multiplying); P is rounded to bf16 for the matrix cores, accumulation
+//    stays float32.
+#include <type_traits>
+
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 
@@ -35,23 +47,30 @@ namespace pkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;       // keys per tile
 constexpr int kMRows = 128;   // (head, row) pairs per workgroup
 constexpr int kThreads = 256;
+// Rescale slack of the online softmax, in powers of two (see the tile loop).
+constexpr float kPrefillSlack = 8.0f;
+constexpr int kWaves = kThreads / 64;
+static_assert(kKT == kWaves * 16, "one cache block per wave and tile");
 
 template <int D>
 struct PrefillShape {
-  static constexpr int kRC = D * 2 / 16;              // 16-byte chunks per key row
-  static constexpr int kKStride = D * 2 + 16;         // LDS bytes per K row
-  static constexpr int kVStride = kKT * 2 + 8;        // LDS bytes per V^T row
-  static constexpr int kKBytes = kKT * kKStride;
-  static constexpr int kVBytes = D * kVStride;
-  static constexpr int kKPerThread = kKT * kRC / kThreads;
-  static constexpr int kVPairsPerThread = (kKT / 2) * kRC / kThreads;
-  static constexpr int kKSteps = D / 16;  // QK^T steps of 16 head dims
-  static constexpr int kND = D / 32;      // PV output blocks of 32 head dims
-  static_assert(kKPerThread >= 1 && kVPairsPerThread >= 1, "tile too small for the workgroup");
+  static constexpr int kRowBytes = D * 2;                // one K or V row (bf16)
+  static constexpr int kRC = kRowBytes / 16;             // 16-byte chunks per row
+  static constexpr int kTileBytes = kKT * kRowBytes;     // one K or V tile
+  static constexpr int kStageBytes = 2 * kTileBytes;     // K then V
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one direct-to-LDS load fills
+  static constexpr int kLoadsPerWave = 16 / kRowsPerLoad;  // per matrix, for the wave's 16 rows
+  static constexpr int kDW = 2 * kLoadsPerWave;          // direct-to-LDS loads per wave and tile
+  static constexpr int kNS = D == 64 ? 4 : 3;            // LDS stages
+  static constexpr int kKSteps = D / 16;                 // QK^T steps of 16 head dims
+  static constexpr int kND = D / 32;                     // PV output blocks of 32 head dims
+  static_assert(kRowsPerLoad * kRC == 64, "one load covers whole rows");
+  static_assert((kNS - 2) * kDW < 64, "vmcnt is six bits");
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -59,16 +78,75 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// LDS reads in one asm block each, completed before the block ends; read i
+// is at base[i] + O.
+template <int O, int N>
+__device__ __forceinline__ void lds_read_b128(const int (&base)[N], u32x4_t (&r)[N]) {
+  static_assert(N == 4 || N == 8, "4 or 8 reads");
+  static_assert(O >= 0 && O < 65536, "ds offset is 16 bits");
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\tds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\tds_read_b128 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "n"(O));
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\tds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\tds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\tds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\tds_read_b128 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "v"(base[4]), "v"(base[5]), "v"(base[6]),
+          "v"(base[7]), "n"(O));
+  }
+}
+
+template <int O, int N>
+__device__ __forceinline__ void lds_read_tr16(const int (&base)[N], u32x2_t (&r)[N]) {
+  static_assert(N == 4 || N == 8, "4 or 8 reads");
+  static_assert(O >= 0 && O < 65536, "ds offset is 16 bits");
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\tds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\tds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "n"(O));
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\tds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\tds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\tds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\tds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "v"(base[4]), "v"(base[5]), "v"(base[6]),
+          "v"(base[7]), "n"(O));
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables) {
   using S = PrefillShape<D>;
-  __shared__ __attribute__((aligned(16))) char smem[S::kKBytes + S::kVBytes];
-  char* k_lds = smem;
-  char* v_lds = smem + S::kKBytes;
+  constexpr int NS = S::kNS;
+  constexpr int RC = S::kRC;
+  constexpr int RB = S::kRowBytes;
+  constexpr int TB = S::kTileBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * S::kStageBytes];
+  const int smem_base = (int)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int QT = kMRows / G;
@@ -99,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
   if (rows_here <= 0) return;
   const int kend = P0 + row0 + rows_here;  // keys [0, kend) are visible to some row
   const int ntiles = (kend + kKT - 1) / kKT;
+  const int nblk = (kend + kBlock - 1) / kBlock;  // table entries that are read
 
   // this lane's query row (column of S^T and O^T)
   const int mrow = wave * 32 + (lane & 31);
@@ -123,71 +202,70 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
     }
   }
 
-  const int32_t* __restrict__ table = a.block_tables + (int64_t)c * a.max_blocks_per_seq;
+  // ---- load side: this wave's block (key rows 16 wave .. 16 wave + 15) of each tile
+  const int32_t* __restrict__ table = tables + (int64_t)c * a.max_blocks_per_seq;
   const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache);
   const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache);
-  const int64_t tile_bytes = (int64_t)kBlock * D * 2;
+  const int64_t tile_bytes = (int64_t)kBlock * RB;  // one (block, kv head) tile of the cache
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
   int local_bad = 0;
-
-  // byte offset in the cache of key position kpos of this kv head, or -1 past kend
-  auto key_off = [&](int kpos) -> int64_t {
-    if (kpos >= kend) return -1;
-    int p = table[kpos >> 4];
+  // byte offset in a cache tile of the global chunk that lands at this lane's
+  // LDS position in load i (row i * rows-per-load + lane / RC, swizzled chunk)
+  int goff[S::kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < S::kLoadsPerWave; ++i) {
+    const int r = i * S::kRowsPerLoad + lane / RC;
+    goff[i] = r * RB + (((lane % RC) ^ (r % RC)) * 16);
+  }
+  // Block of this wave in tile kt (uniform).  Blocks past the visible keys
+  // read block 0 (their rows are never used: K rows past the keys are masked,
+  // and the V rows of the last tile past the keys are zeroed in LDS).
+  auto table_entry = [&](int kt) -> int {
+    const int jb = kt * kWaves + wave;
+    int p = jb < nblk ? table[jb] : 0;
     if (p < 0 || p >= a.num_blocks) {
       local_bad = 1;
       p = 0;
     }
-    return (int64_t)p * blk_stride + (int64_t)g * tile_bytes + (int64_t)(kpos & 15) * D * 2;
+    return p;
   };
-  auto gload_chunk = [&](const char* base, int64_t off, int ch) -> Chunk {
-    if (off < 0) {
-      Chunk z;
-      z.w[0] = z.w[1] = z.w[2] = z.w[3] = 0u;
-      return z;
+  auto issue = [&](int kt, int p) {  // direct-to-LDS loads of this wave's rows of tile kt (block p)
+    char* kdst = smem + (kt % NS) * S::kStageBytes + wave * 16 * RB;
+    const int64_t boff = (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
+    const char* kb = kc + boff;
+    const char* vb = vc + boff;
+#pragma unroll
+    for (int i = 0; i < S::kLoadsPerWave; ++i) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + goff[i]),
+                                       (__attribute__((address_space(3))) void*)(kdst + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + goff[i]),
+                                       (__attribute__((address_space(3))) void*)(kdst + TB + i * 1024), 16, 0, 0);
     }
-    return load_chunk(base + off + ch * 16);
   };
 
-  Chunk kreg[S::kKPerThread];
-  Chunk vreg[S::kVPairsPerThread][2];
-  auto gload = [&](int kt) {
+  // ---- compute side: per-lane LDS byte offsets of the operands, without the
+  // stage and without the key-block part that is the same for every lane
+  // (that part goes into the reads' immediate offset).
+  // K operand of step kk for key block nb: key row nb*32 + lane%32, dims 16 kk + 8 half.
+  const int kr = lane & 31;
+  int koff[S::kKSteps];
 #pragma unroll
-    for (int r = 0; r < S::kKPerThread; ++r) {
-      const int q = tid + kThreads * r;
-      const int key = q / S::kRC, ch = q % S::kRC;
-      kreg[r] = gload_chunk(kc, key_off(kt * kKT + key), ch);
+  for (int kk = 0; kk < S::kKSteps; ++kk) koff[kk] = kr * RB + (((2 * kk + half) ^ (kr % RC)) * 16);
+  // V^T operand (transpose reads) of step (nb, s), read r, dim block nd: source lane addresses
+  // key nb*32 + 16 s + 8 r + vkey, dims 32 nd + vdim + 0..3; the chunk swizzle of that row only
+  // depends on 8 r + vkey (nb*32 + 16 s is a multiple of the chunks per row).
+  const int grp = lane >> 4;
+  const int vkey = 4 * (grp >> 1) + ((lane & 15) >> 2);
+  const int vdim = 16 * (grp & 1) + 4 * (lane & 3);
+  constexpr int NR = 2 * S::kND;  // transpose reads per PV step
+  int voff[NR];
+#pragma unroll
+  for (int nd = 0; nd < S::kND; ++nd)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int key = 8 * r + vkey, dim = 32 * nd + vdim;
+      voff[2 * nd + r] = TB + key * RB + (((dim >> 3) ^ (key % RC)) * 16) + (dim & 7) * 2;
     }
-#pragma unroll
-    for (int r = 0; r < S::kVPairsPerThread; ++r) {
-      const int q = tid + kThreads * r;
-      const int kp = (q & 15) + 16 * (q / (16 * S::kRC));
-      const int ch = (q >> 4) % S::kRC;
-      vreg[r][0] = gload_chunk(vc, key_off(kt * kKT + 2 * kp), ch);
-      vreg[r][1] = gload_chunk(vc, key_off(kt * kKT + 2 * kp + 1), ch);
-    }
-  };
-  auto swrite = [&]() {
-#pragma unroll
-    for (int r = 0; r < S::kKPerThread; ++r) {
-      const int q = tid + kThreads * r;
-      const int key = q / S::kRC, ch = q % S::kRC;
-      store_chunk(k_lds + key * S::kKStride + ch * 16, kreg[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < S::kVPairsPerThread; ++r) {
-      const int q = tid + kThreads * r;
-      const int kp = (q & 15) + 16 * (q / (16 * S::kRC));
-      const int ch = (q >> 4) % S::kRC;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = vreg[r][0].w[w], hi = vreg[r][1].w[w];
-        const int dim = 8 * ch + 2 * w;
-        *reinterpret_cast<uint32_t*>(v_lds + dim * S::kVStride + kp * 4) = (lo & 0xffffu) | (hi << 16);
-        *reinterpret_cast<uint32_t*>(v_lds + (dim + 1) * S::kVStride + kp * 4) = (lo >> 16) | (hi & 0xffff0000u);
-      }
-    }
-  };
 
   float m_run = kMaxInit, l_run = 0.0f;
   f32x16_t oacc[S::kND];
@@ -197,36 +275,71 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
     for (int v = 0; v < 16; ++v) oacc[nd][v] = 0.0f;
   const float sl2 = a.scale_log2;
 
-  gload(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();
-    swrite();
-    __syncthreads();
-    if (kt + 1 < ntiles) gload(kt + 1);
+  // prologue: tiles 0 .. NS-2 in flight (past the last tile: zero rows, so every
+  // iteration finds the same number of loads outstanding)
+  int pnext = table_entry(0);
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) {
+    const int p = pnext;
+    pnext = table_entry(t + 1);
+    issue(t, p);
+  }
 
-    f32x16_t st[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) st[nb][v] = 0.0f;
-      const char* krow = k_lds + (nb * 32 + (lane & 31)) * S::kKStride + 16 * half;
-#pragma unroll
-      for (int kk = 0; kk < S::kKSteps; ++kk) {
-        const Chunk ch = load_chunk(krow + kk * 32);
-        st[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ch.w[0], ch.w[1], ch.w[2], ch.w[3]), qop[kk],
-                                                         st[nb], 0, 0, 0);
+  // Tile kt: wait for its loads, start the loads of tile kt + NS - 1, then
+  // S^T = K Q^T, the online softmax and O^T += V^T P^T.  MASK: the tile holds
+  // keys past some row's position (diagonal tiles; the last one also holds
+  // keys past every row's, whose V rows are zeroed first).
+  auto tile = [&](auto mask_tag, int kt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // this wave's loads of tile kt are done once at most NS-2 tiles' loads remain;
+    // the barrier then makes every wave's part visible and frees the stage of kt-1
+    wait_vmcnt_le<(NS - 2) * S::kDW>();
+    __builtin_amdgcn_s_barrier();
+    {
+      const int p = pnext;
+      pnext = table_entry(kt + NS);
+      issue(kt + NS - 1, p);
+    }
+    const int sbase = smem_base + (kt % NS) * S::kStageBytes;
+    if constexpr (MASK) {
+      const int r0 = kend - kt * kKT;  // rows [r0, 64) of the tile are past every row's keys
+      if (r0 < kKT) {
+        char* vt = smem + (kt % NS) * S::kStageBytes + TB;
+        for (int idx = tid; idx < (kKT - r0) * RC; idx += kThreads)
+          *reinterpret_cast<uint4*>(vt + (r0 + idx / RC) * RB + (idx % RC) * 16) = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       }
     }
 
-    // scale, causal mask (select), row max over this lane and lane ^ 32
-    const bool diag = kt * kKT + kKT - 1 > P0 + row0;
+    f32x16_t st[2];
+    {
+      int kb[S::kKSteps];
+#pragma unroll
+      for (int kk = 0; kk < S::kKSteps; ++kk) kb[kk] = sbase + koff[kk];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st[nb][v] = 0.0f;
+        u32x4_t kv[S::kKSteps];
+        if (nb == 0) lds_read_b128<0>(kb, kv);
+        else lds_read_b128<32 * RB>(kb, kv);
+#pragma unroll
+        for (int kk = 0; kk < S::kKSteps; ++kk)
+          st[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[kk]), qop[kk], st[nb], 0,
+                                                           0, 0);
+      }
+    }
+
+    // scale, causal mask (select, diagonal tiles only), row max over this lane and lane ^ 32
     float mx = -__builtin_inff();
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float x = st[nb][v] * sl2;
-        if (diag) {
+        if constexpr (MASK) {
           const int kpos = kt * kKT + nb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
           x = kpos > qpos ? -__builtin_inff() : x;
         }
@@ -234,9 +347,20 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
         mx = fmaxf(mx, x);
       }
     mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - mn);
-    m_run = mn;
+    // Lazy rescale: the running max moves (and O, l are rescaled) only when a
+    // score exceeds it by more than 2^8, which bounds every P by 256; the
+    // final normalisation makes the stale max exact.
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m_run + kPrefillSlack) != 0, 0)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int nd = 0; nd < S::kND; ++nd)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[nd][v] *= alpha;
+    }
+    const float mn = m_run;
 
     uint32_t pk[2][8];
     float ps = 0.0f;
@@ -249,29 +373,34 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
         ps += p0 + p1;
         pk[nb][u] = pack_bf16x2(p0, p1);
       }
-    l_run = l_run * alpha + ps;
-#pragma unroll
-    for (int nd = 0; nd < S::kND; ++nd)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[nd][v] *= alpha;
+    l_run += ps;
 
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bf16x8_t bop = as_bf16x8(pk[nb][4 * s], pk[nb][4 * s + 1], pk[nb][4 * s + 2], pk[nb][4 * s + 3]);
-        const int koff0 = nb * 32 + 16 * s + 4 * half;
+        int vb[NR];
 #pragma unroll
-        for (int nd = 0; nd < S::kND; ++nd) {
-          const char* vrow = v_lds + (nd * 32 + (lane & 31)) * S::kVStride;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + koff0 * 2);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (koff0 + 8) * 2);
-          oacc[nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo.x, lo.y, hi.x, hi.y), bop, oacc[nd], 0, 0,
-                                                             0);
-        }
+        for (int i = 0; i < NR; ++i) vb[i] = sbase + voff[i];
+        u32x2_t vv[NR];
+        if (nb == 0 && s == 0) lds_read_tr16<0>(vb, vv);
+        else if (nb == 0) lds_read_tr16<16 * RB>(vb, vv);
+        else if (s == 0) lds_read_tr16<32 * RB>(vb, vv);
+        else lds_read_tr16<48 * RB>(vb, vv);
+#pragma unroll
+        for (int nd = 0; nd < S::kND; ++nd)
+          oacc[nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(vv[2 * nd].x, vv[2 * nd].y, vv[2 * nd + 1].x, vv[2 * nd + 1].y), bop, oacc[nd], 0, 0, 0);
       }
-  }
+  };
+  // tiles with no key past any row's position, then the diagonal ones
+  const int nfull = min(ntiles, (P0 + row0 + 1) / kKT);
+  for (int kt = 0; kt < nfull; ++kt) tile(std::false_type{}, kt);
+  for (int kt = nfull; kt < ntiles; ++kt) tile(std::true_type{}, kt);
 
+  // no direct-to-LDS load may still be writing when the workgroup's LDS is released
+  wait_vmcnt_le<0>();
   const int any_bad = __syncthreads_or(local_bad);
   const float l_tot = l_run + shfl_xor_f32(l_run, 32);
   if (!row_ok) return;
@@ -299,10 +428,12 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   switch (a.head_dim) {
     case 64:
-      hipLaunchKernelGGL(prefill_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(prefill_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+                         a.block_tables);
       break;
     case 128:
-      hipLaunchKernelGGL(prefill_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(prefill_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+                         a.block_tables);
       break;
     default:
       return hipErrorInvalidValue;
