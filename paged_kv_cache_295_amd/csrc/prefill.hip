@@ -57,6 +57,10 @@ constexpr float kPrefillSlack = 8.0f;
 constexpr int kWaves = kThreads / 64;
 static_assert(kKT == kWaves * 16, "one cache block per wave and tile");
 
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 3
+#endif
+
 template <int D>
 struct PrefillShape {
   static constexpr int kRowBytes = D * 2;                // one K or V row (bf16)
@@ -66,7 +70,7 @@ struct PrefillShape {
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one direct-to-LDS load fills
   static constexpr int kLoadsPerWave = 16 / kRowsPerLoad;  // per matrix, for the wave's 16 rows
   static constexpr int kDW = 2 * kLoadsPerWave;          // direct-to-LDS loads per wave and tile
-  static constexpr int kNS = D == 64 ? 4 : 3;            // LDS stages
+  static constexpr int kNS = PKV_PREFILL_STAGES;         // LDS stages
   static constexpr int kKSteps = D / 16;                 // QK^T steps of 16 head dims
   static constexpr int kND = D / 32;                     // PV output blocks of 32 head dims
   static_assert(kRowsPerLoad * kRC == 64, "one load covers whole rows");
