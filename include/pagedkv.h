@@ -150,6 +150,40 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
                       size_t workspace_bytes, void* hip_stream);
 
 /*
+ * paged_attn_decode_shared_prefix -- a decode step (as paged_attn_decode) for
+ * a batch of sequences that all start with the same prompt prefix held once
+ * in shared physical blocks.  (ainews.alishangtian.com article, section
+ * "PagedAttention": requests with a common prefix reference the same physical
+ * blocks; caffein.top essay, section on the prefix tree.)  The prefix is
+ * attended once for the whole batch as a dense matrix-core problem (every
+ * query of the batch against the prefix keys, read from HBM once); each
+ * sequence's own tokens then continue from that state, and the log-sum-exp
+ * merge makes the result equal to attention over the concatenated context.
+ *
+ *   q, out            [num_seqs][num_q_heads][head_dim]
+ *   prefix_blocks     int32 [prefix_len / 16]: the shared prefix's blocks, in order
+ *   prefix_len        tokens of the prefix, a multiple of 16 (0: plain decode)
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]: each sequence's
+ *                     blocks after the prefix (its logical tokens prefix_len ..)
+ *   context_lens      int32 [num_seqs] (device): tokens after the prefix,
+ *                     including the new one; 0 gives attention over the prefix alone
+ *   workspace         device scratch of at least
+ *                     paged_attn_decode_shared_prefix_workspace_bytes(...) bytes
+ *
+ * Sequence s attends to prefix tokens 0 .. prefix_len-1 followed by its own
+ * context_lens[s] tokens.  bfloat16 caches only (PKV_ERR_UNSUPPORTED for
+ * float32).  Device-side contract and NaN behaviour as paged_attn_decode (the
+ * balanced split; a prefix block id out of range makes every output NaN).
+ */
+size_t paged_attn_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                       int32_t head_dim, int32_t prefix_len);
+int paged_attn_decode_shared_prefix(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                                    const void* v_cache, const pkv_cache_desc* cache, const int32_t* prefix_blocks,
+                                    int32_t prefix_len, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, float scale, void* out, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream);
+
+/*
  * paged_attn_prefill_chunk -- causal attention for chunks of prompts whose
  * K/V (including the chunk's own rows) are already in the cache.
  * (caffein.top essay, section on chunked prefill; "Part 47", section 2.1 for
@@ -181,7 +215,7 @@ const char* pkv_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION ((1 << 16) | 0)
+#define PKV_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

@@ -169,6 +169,26 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype, gather
     return out
 
 
+def decode_shared_prefix(q, k_cache, v_cache, prefix_blocks, block_tables, context_lens, scale, dtype):
+    """Decode for sequences that all start with one prompt prefix stored once.
+
+    ainews.alishangtian.com article on inference engines, section
+    "PagedAttention": requests with a common prefix reference the same physical
+    blocks.  Sequence s's context is the prefix -- the 16-token blocks
+    prefix_blocks, in order -- followed by its own context_lens[s] tokens listed
+    in block_tables[s]; the result is plain attention over that whole context
+    (decode above), whatever order the work is done in.
+    """
+    prefix_blocks = np.asarray(prefix_blocks, dtype=np.int64).reshape(-1)
+    tables = np.asarray(block_tables)
+    n_pre = prefix_blocks.shape[0]
+    full = np.empty((tables.shape[0], n_pre + tables.shape[1]), dtype=np.int64)
+    full[:, :n_pre] = prefix_blocks
+    full[:, n_pre:] = tables
+    lens = np.asarray(context_lens, dtype=np.int64) + n_pre * BLOCK_SIZE
+    return decode(q, k_cache, v_cache, full, lens, scale, dtype)
+
+
 def prefill_chunk(q_chunk, chunk_start, k_cache, v_cache, block_tables, context_lens, scale, dtype,
                   gather_fn=None):
     """Causal attention of each prefill chunk's rows over its cached context.

@@ -16,6 +16,7 @@ import os
 __all__ = [
     "PagedKVError", "load_library", "paged_kv_write", "paged_attn_decode", "paged_attn_prefill_chunk",
     "decode_workspace_bytes", "decode_split_waves", "library_path", "BLOCK_SIZE",
+    "paged_attn_decode_shared_prefix", "shared_prefix_workspace_bytes",
 ]
 
 BLOCK_SIZE = 16
@@ -62,6 +63,11 @@ def load_library():
     lib.paged_attn_decode_workspace_bytes.restype = sz
     lib.paged_attn_decode.argtypes = [vp, i32, i32, vp, vp, cdp, vp, i32, vp, i32, f32, vp, i32, vp, sz, vp]
     lib.paged_attn_decode.restype = ctypes.c_int
+    lib.paged_attn_decode_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.paged_attn_decode_shared_prefix_workspace_bytes.restype = sz
+    lib.paged_attn_decode_shared_prefix.argtypes = [vp, i32, i32, vp, vp, cdp, vp, i32, vp, i32, vp, f32, vp, vp, sz,
+                                                    vp]
+    lib.paged_attn_decode_shared_prefix.restype = ctypes.c_int
     lib.paged_attn_prefill_chunk.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp]
     lib.paged_attn_prefill_chunk.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
@@ -179,6 +185,39 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
                                int(max_context_len), float(scale), _ptr(out), int(partition_tokens), ws_ptr,
                                ws_bytes, _stream(stream))
     _check(st, "paged_attn_decode")
+    return out
+
+
+def shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, prefix_len) -> int:
+    return int(load_library().paged_attn_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                                              head_dim, prefix_len))
+
+
+def paged_attn_decode_shared_prefix(q, k_cache, v_cache, prefix_blocks, block_tables, context_lens, scale, out,
+                                    workspace=None, stream=None):
+    """Decode for sequences that share the prefix held in prefix_blocks (int32 [P]; P*16 tokens):
+    sequence s attends to the prefix and then to its own context_lens[s] tokens in block_tables[s]."""
+    lib = load_library()
+    _same_dtype(q, out, k_cache, v_cache)
+    desc = _cache_desc(k_cache)
+    B, hq, d = q.shape
+    if out.shape != q.shape or d != desc.head_dim:
+        raise ValueError("q/out must be [B, Hq, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables [B, max_blocks], context_lens [B]")
+    if prefix_blocks.dim() != 1:
+        raise ValueError("prefix_blocks [num_prefix_blocks]")
+    prefix_len = prefix_blocks.shape[0] * BLOCK_SIZE
+    need = shared_prefix_workspace_bytes(B, hq, desc.num_kv_heads, d, prefix_len)
+    if workspace is None:
+        workspace = _torch().empty(max(need, 1), dtype=_torch().uint8, device=q.device)
+    pb = _i32(prefix_blocks, "prefix_blocks") if prefix_len else None
+    st = lib.paged_attn_decode_shared_prefix(_ptr(q), B, hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), pb,
+                                             prefix_len, _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                             _i32(context_lens, "context_lens"), float(scale), _ptr(out),
+                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream(stream))
+    _check(st, "paged_attn_decode_shared_prefix")
     return out
 
 

@@ -39,6 +39,35 @@ size_t partition_workspace(int32_t num_seqs, int32_t hq, int32_t head_dim, int32
   return (size_t)num_seqs * hq * max_parts * ((size_t)head_dim + 2) * sizeof(float);
 }
 
+// Shared prefix: pieces of the prefix for the matrix-core kernel, enough to give
+// each of the 256 compute units about one workgroup (128 rows x 64-key tiles).
+struct PrefixSplit {
+  int32_t splits;
+  int32_t split_tokens;
+};
+
+PrefixSplit prefix_split(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t prefix_len) {
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t row_tiles = (num_seqs * G + 127) / 128;
+  const int64_t wgs = row_tiles * num_kv_heads;
+  const int64_t tiles = (prefix_len + 63) / 64;
+  int64_t want = (256 + wgs - 1) / wgs;
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  const int64_t per = (tiles + want - 1) / want;
+  PrefixSplit r;
+  r.split_tokens = (int32_t)(per * 64);
+  r.splits = (int32_t)((prefix_len + r.split_tokens - 1) / r.split_tokens);
+  return r;
+}
+
+size_t prefix_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t prefix_len) {
+  if (prefix_len <= 0) return 0;
+  const PrefixSplit ps = prefix_split(num_seqs, num_q_heads, num_kv_heads, prefix_len);
+  return (size_t)ps.splits * num_seqs * num_q_heads * ((size_t)head_dim + 2) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +158,96 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
   a.max_parts = (int32_t)max_parts64;
   a.scale_log2 = scale * kLog2eHost;
   a.balanced_waves = balanced ? balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads)) : 0;
+  return from_hip(launch_decode(a, as_stream(hip_stream)));
+}
+
+size_t paged_attn_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                       int32_t head_dim, int32_t prefix_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || prefix_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  const size_t pre = prefix_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, prefix_len);
+  const size_t pre_aligned = (pre + 255) / 256 * 256;
+  return pre_aligned + balanced_workspace(num_q_heads, num_kv_heads, head_dim);
+}
+
+int paged_attn_decode_shared_prefix(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                                    const void* v_cache, const pkv_cache_desc* cache, const int32_t* prefix_blocks,
+                                    int32_t prefix_len, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, float scale, void* out, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (cache->dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;  // the prefix runs on the matrix cores
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
+  if (prefix_len < 0 || prefix_len % PKV_BLOCK_SIZE != 0 || prefix_len >= (1 << 30)) return PKV_ERR_SHAPE;
+  if (prefix_len > 0 && !prefix_blocks) return PKV_ERR_NULL;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  const size_t pre = prefix_workspace(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim, prefix_len);
+  const size_t pre_aligned = (pre + 255) / 256 * 256;
+  const size_t need = pre_aligned + balanced_workspace(num_q_heads, cache->num_kv_heads, cache->head_dim);
+  if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  const float sl2 = scale * kLog2eHost;
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* pre_o = reinterpret_cast<float*>(ws);
+  PrefixSplit ps{0, 0};
+  if (prefix_len > 0) {
+    ps = prefix_split(num_seqs, num_q_heads, cache->num_kv_heads, prefix_len);
+    float* pre_ml = pre_o + (size_t)ps.splits * num_seqs * num_q_heads * cache->head_dim;
+    PrefillArgs pa{};
+    pa.q = q;
+    pa.k_cache = k_cache;
+    pa.v_cache = v_cache;
+    pa.block_tables = prefix_blocks;
+    pa.num_chunks = num_seqs;
+    pa.chunk_len_max = 1;
+    pa.num_q_heads = num_q_heads;
+    pa.num_kv_heads = cache->num_kv_heads;
+    pa.head_dim = cache->head_dim;
+    pa.num_blocks = cache->num_blocks;
+    pa.max_blocks_per_seq = prefix_len / PKV_BLOCK_SIZE;
+    pa.scale_log2 = sl2;
+    pa.prefix_len = prefix_len;
+    pa.split_tokens = ps.split_tokens;
+    pa.num_splits = ps.splits;
+    pa.part_o = pre_o;
+    pa.part_ml = pre_ml;
+    st = from_hip(launch_prefix_mfma(pa, as_stream(hip_stream)));
+    if (st != PKV_OK) return st;
+  }
+  DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.chunk_start = nullptr;
+  const size_t dec = balanced_workspace(num_q_heads, cache->num_kv_heads, cache->head_dim);
+  a.part_o = reinterpret_cast<float*>(ws + pre_aligned);
+  a.part_ml = reinterpret_cast<float*>(ws + pre_aligned + dec / ((size_t)cache->head_dim + 2) * cache->head_dim);
+  a.num_seqs = num_seqs;
+  a.rows_per_seq = 1;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.dtype = cache->dtype;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.partition_tokens = max_blocks_per_seq * PKV_BLOCK_SIZE;
+  a.max_parts = 1;
+  a.scale_log2 = sl2;
+  a.balanced_waves = balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads));
+  if (prefix_len > 0) {
+    a.init_o = pre_o;
+    a.init_ml = pre_o + (size_t)ps.splits * num_seqs * num_q_heads * cache->head_dim;
+    a.init_splits = ps.splits;
+  }
   return from_hip(launch_decode(a, as_stream(hip_stream)));
 }
 

@@ -303,13 +303,45 @@ struct Segment {
     PV<T, NP, CPL, GB>::apply(sc, vz, acc);
   }
 
+  // Start from the attention state of a shared prefix: the a.init_splits
+  // partials of rows [row, row + GB) (sequence * Hq + head) merged into token
+  // group 0 (the other groups start empty; merge_groups combines them later).
+  __device__ __forceinline__ void seed(const DecodeArgs& a, int64_t row) {
+    if (tg != 0) return;
+    const int64_t split_stride = (int64_t)a.num_seqs * a.num_q_heads;
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      float M = -__builtin_inff();
+      for (int sp = 0; sp < a.init_splits; ++sp) {
+        const float ms = a.init_ml[(sp * split_stride + row + h) * 2];
+        bad_block |= ms != ms;
+        M = fmaxf(M, ms);
+      }
+      float lam = 0.0f;
+      for (int sp = 0; sp < a.init_splits; ++sp) {
+        const int64_t r = sp * split_stride + row + h;
+        const float f = fast_exp2(a.init_ml[r * 2] - M);
+        lam = fmaf(f, a.init_ml[r * 2 + 1], lam);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[h][c][e] = fmaf(f, a.init_o[r * D + (c * LPT + li) * EPC + e], acc[h][c][e]);
+      }
+      m[h] = M;
+      l[h] = lam;
+    }
+  }
+
   // Attend the GB query rows at qrow (head h0 of the row) over tokens
   // [16 * blk0, end) of one sequence, whose blocks blk0 .. blk0 + nblk - 1 are
-  // listed at table[0 .. nblk - 1], for kv head g.
+  // listed at table[0 .. nblk - 1], for kv head g; seed_row >= 0 starts from
+  // the shared-prefix state of that row (see seed).
   __device__ __forceinline__ void run(const DecodeArgs& a, const T* __restrict__ qrow,
-                                      const int32_t* __restrict__ table, int g, int blk0, int nblk, int end) {
+                                      const int32_t* __restrict__ table, int g, int blk0, int nblk, int end,
+                                      int64_t seed_row = -1) {
     load_q(qrow);
     reset();
+    if (seed_row >= 0) seed(a, seed_row);
     const int64_t blk_stride = kTileBytes * a.num_kv_heads;
     const int num_blocks = a.num_blocks;
     // Table entries are uniform: scalar loads (the table is a read-only,
@@ -642,7 +674,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
     const int g = k / hsubs, hs = k - g * hsubs;
     const int h0 = g * G + hs * GB;
     const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)s * a.num_q_heads + h0) * D;
-    seg.run(a, qrow, tables + (int64_t)s * a.max_blocks_per_seq + j, g, j, jn - j, min(L, jn * kBlock));
+    seg.run(a, qrow, tables + (int64_t)s * a.max_blocks_per_seq + j, g, j, jn - j, min(L, jn * kBlock),
+            (a.init_o != nullptr && j == 0) ? (int64_t)s * a.num_q_heads + h0 : -1);
     seg.merge_groups();
     if (j == 0 && jn == nb) {
       seg.store_out(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D);
@@ -687,6 +720,33 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
   T* outp = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D;
 
   const int L = a.context_lens[s];
+  if (L == 0 && a.init_o != nullptr) {  // nothing after the shared prefix: its state alone
+    const int64_t split_stride = (int64_t)B * a.num_q_heads;
+    const int64_t row = (int64_t)s * a.num_q_heads + h0;
+    for (int h = 0; h < GB; ++h) {
+      float M = -__builtin_inff();
+      bool nan = false;
+      for (int sp = 0; sp < a.init_splits; ++sp) {
+        const float ms = a.init_ml[(sp * split_stride + row + h) * 2];
+        nan |= ms != ms;
+        M = fmaxf(M, ms);
+      }
+      float lam = 0.0f, o[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+      for (int sp = 0; sp < a.init_splits; ++sp) {
+        const int64_t r = sp * split_stride + row + h;
+        const float f = fast_exp2(a.init_ml[r * 2] - M);
+        lam = fmaf(f, a.init_ml[r * 2 + 1], lam);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] = fmaf(f, a.init_o[r * D + lane + e * kWave], o[e]);
+      }
+      const float inv = nan ? __builtin_nanf("") : 1.0f / lam;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) outp[h * D + lane + e * kWave] = (T)(o[e] * inv);
+    }
+    return;
+  }
   if (L < 0 || L > cap || L == 0) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
     for (int i = lane; i < GB * D; i += kWave) outp[i] = (T)fill;

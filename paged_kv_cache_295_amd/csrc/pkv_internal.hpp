@@ -49,6 +49,13 @@ struct DecodeArgs {
   // > 0: balanced split over this many waves (decode only); part_o / part_ml
   // then hold [waves][2][heads per wave][D] and [waves][2][heads per wave][2]
   int32_t balanced_waves;
+  // Shared prefix (balanced split only; init_o == nullptr otherwise): every
+  // stream's first segment starts from the attention state of the prefix,
+  // given as init_splits partials [split][seq][Hq][D] (unnormalised) and
+  // [split][seq][Hq][2] (max in log2 units, sum).
+  const float* init_o;
+  const float* init_ml;
+  int32_t init_splits;
 };
 
 struct PrefillArgs {
@@ -67,12 +74,23 @@ struct PrefillArgs {
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   float scale_log2;
+  // Shared-prefix mode (prefix_len > 0): the rows are the num_chunks decode
+  // queries q [num_chunks][Hq][D]; keys are the prefix_len tokens of
+  // block_tables[0 .. prefix_len / 16), split into pieces of split_tokens;
+  // each piece writes (m, l, o) partials to part_o [piece][seq][Hq][D] and
+  // part_ml [piece][seq][Hq][2].
+  int32_t prefix_len;
+  int32_t split_tokens;
+  int32_t num_splits;
+  float* part_o;
+  float* part_ml;
 };
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 // Returns hipErrorInvalidValue if no instantiation covers the shape.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefix_mfma(const PrefillArgs& a, hipStream_t stream);
 
 // Heads processed together by one wave for a GQA group of size g.
 constexpr int heads_per_wave(int g) {

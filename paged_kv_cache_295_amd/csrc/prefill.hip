@@ -138,7 +138,11 @@ __device__ __forceinline__ void wait_vmcnt_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
 }
 
-template <int D>
+// PREFIX = false: chunked prefill (rows = chunk rows x G heads of one kv head,
+// keys 0 .. row position, causal).  PREFIX = true: the shared prefix of a
+// batch of decode queries (rows = (sequence, head) pairs of one kv head, keys
+// = one piece of the prefix, no causal mask), written as (m, l, o) partials.
+template <int D, bool PREFIX>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables) {
   using S = PrefillShape<D>;
   constexpr int NS = S::kNS;
@@ -153,56 +157,82 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int QT = kMRows / G;
-  const int n_mt = (a.chunk_len_max + QT - 1) / QT;
-  const int npair = a.num_chunks * a.num_kv_heads;
   const int id = blockIdx.x;
-  const int pair = id % npair;
-  const int mt = n_mt - 1 - id / npair;  // the longest row tiles start first
-  const int c = pair / a.num_kv_heads;
-  const int g = pair - c * a.num_kv_heads;
-
-  const int P0 = a.chunk_start[c];
-  const int L = a.context_lens[c];
-  const int n = L - P0;
-  const bool bad_chunk = P0 < 0 || n < 0 || L > a.max_blocks_per_seq * kBlock || n > a.chunk_len_max;
-  const int row0 = mt * QT;
-  __bf16* __restrict__ out = reinterpret_cast<__bf16*>(a.out);
-  if (bad_chunk) {
-    const int rows = min(QT, a.chunk_len_max - row0);
-    for (int idx = tid; idx < rows * G * D; idx += kThreads) {
-      const int r = idx / (G * D), rem = idx - r * G * D;
-      out[((int64_t)(c * a.chunk_len_max + row0 + r) * a.num_q_heads + g * G) * D + rem] =
-          (__bf16)__builtin_nanf("");
-    }
-    return;
-  }
-  const int rows_here = min(QT, n - row0);
-  if (rows_here <= 0) return;
-  const int kend = P0 + row0 + rows_here;  // keys [0, kend) are visible to some row
-  const int ntiles = (kend + kKT - 1) / kKT;
-  const int nblk = (kend + kBlock - 1) / kBlock;  // table entries that are read
-
   // this lane's query row (column of S^T and O^T)
   const int mrow = wave * 32 + (lane & 31);
-  const int hl = mrow / QT;
-  const int qi = row0 + (mrow - hl * QT);
-  const bool row_ok = hl < G && qi < n;
-  const int qpos = P0 + qi;
-  const int head = g * G + hl;
+  __bf16* __restrict__ out = reinterpret_cast<__bf16*>(a.out);
+
+  int c, g, kt0, kend, ntiles, nblk, mask_from, qpos, head;
+  bool row_ok;
+  const __bf16* qrow;
+  int64_t part_row = 0;  // PREFIX: (piece, sequence, head) row of the partials
+  int64_t out_row = 0;   // prefill: (chunk, row) of q and out
+  if constexpr (PREFIX) {
+    const int sp = id % a.num_splits;
+    const int t = id / a.num_splits;
+    g = t % a.num_kv_heads;
+    const int mt = t / a.num_kv_heads;
+    const int k0 = sp * a.split_tokens;
+    kend = min(a.prefix_len, k0 + a.split_tokens);
+    kt0 = k0 / kKT;
+    ntiles = (kend + kKT - 1) / kKT;
+    nblk = (kend + kBlock - 1) / kBlock;
+    mask_from = kend;  // keys past the piece (its last tile only) are masked
+    qpos = kend - 1;
+    const int rr = mt * kMRows + mrow;
+    const int seq = rr / G, hl = rr - seq * G;
+    row_ok = seq < a.num_chunks;
+    head = g * G + hl;
+    c = 0;  // the prefix is row 0 of the table
+    qrow = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)(row_ok ? seq : 0) * a.num_q_heads + head) * D;
+    part_row = ((int64_t)sp * a.num_chunks + seq) * a.num_q_heads + head;
+  } else {
+    const int QT = kMRows / G;
+    const int n_mt = (a.chunk_len_max + QT - 1) / QT;
+    const int npair = a.num_chunks * a.num_kv_heads;
+    const int pair = id % npair;
+    const int mt = n_mt - 1 - id / npair;  // the longest row tiles start first
+    c = pair / a.num_kv_heads;
+    g = pair - c * a.num_kv_heads;
+
+    const int P0 = a.chunk_start[c];
+    const int L = a.context_lens[c];
+    const int n = L - P0;
+    const bool bad_chunk = P0 < 0 || n < 0 || L > a.max_blocks_per_seq * kBlock || n > a.chunk_len_max;
+    const int row0 = mt * QT;
+    if (bad_chunk) {
+      const int rows = min(QT, a.chunk_len_max - row0);
+      for (int idx = tid; idx < rows * G * D; idx += kThreads) {
+        const int r = idx / (G * D), rem = idx - r * G * D;
+        out[((int64_t)(c * a.chunk_len_max + row0 + r) * a.num_q_heads + g * G) * D + rem] =
+            (__bf16)__builtin_nanf("");
+      }
+      return;
+    }
+    const int rows_here = min(QT, n - row0);
+    if (rows_here <= 0) return;
+    kend = P0 + row0 + rows_here;  // keys [0, kend) are visible to some row
+    kt0 = 0;
+    ntiles = (kend + kKT - 1) / kKT;
+    nblk = (kend + kBlock - 1) / kBlock;  // table entries that are read
+    mask_from = P0 + row0 + 1;            // the first key some row may not see
+    const int hl = mrow / QT;
+    const int qi = row0 + (mrow - hl * QT);
+    row_ok = hl < G && qi < n;
+    qpos = P0 + qi;
+    head = g * G + hl;
+    out_row = (int64_t)c * a.chunk_len_max + qi;
+    qrow = reinterpret_cast<const __bf16*>(a.q) + (out_row * a.num_q_heads + head) * D;
+  }
 
   bf16x8_t qop[S::kKSteps];
-  {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) +
-                         ((int64_t)(c * a.chunk_len_max + qi) * a.num_q_heads + head) * D;
 #pragma unroll
-    for (int kk = 0; kk < S::kKSteps; ++kk) {
-      if (row_ok) {
-        const Chunk ch = load_chunk(qrow + kk * 16 + 8 * half);
-        qop[kk] = as_bf16x8(ch.w[0], ch.w[1], ch.w[2], ch.w[3]);
-      } else {
-        qop[kk] = as_bf16x8(0u, 0u, 0u, 0u);
-      }
+  for (int kk = 0; kk < S::kKSteps; ++kk) {
+    if (row_ok) {
+      const Chunk ch = load_chunk(qrow + kk * 16 + 8 * half);
+      qop[kk] = as_bf16x8(ch.w[0], ch.w[1], ch.w[2], ch.w[3]);
+    } else {
+      qop[kk] = as_bf16x8(0u, 0u, 0u, 0u);
     }
   }
 
@@ -281,12 +311,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
 
   // prologue: tiles 0 .. NS-2 in flight (past the last tile: zero rows, so every
   // iteration finds the same number of loads outstanding)
-  int pnext = table_entry(0);
+  int pnext = table_entry(kt0);
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t) {
     const int p = pnext;
-    pnext = table_entry(t + 1);
-    issue(t, p);
+    pnext = table_entry(kt0 + t + 1);
+    issue(kt0 + t, p);
   }
 
   // Tile kt: wait for its loads, start the loads of tile kt + NS - 1, then
@@ -399,27 +429,43 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
       }
   };
   // tiles with no key past any row's position, then the diagonal ones
-  const int nfull = min(ntiles, (P0 + row0 + 1) / kKT);
-  for (int kt = 0; kt < nfull; ++kt) tile(std::false_type{}, kt);
-  for (int kt = nfull; kt < ntiles; ++kt) tile(std::true_type{}, kt);
+  const int nfull = min(ntiles, mask_from / kKT);
+  for (int kt = kt0; kt < nfull; ++kt) tile(std::false_type{}, kt);
+  for (int kt = max(kt0, nfull); kt < ntiles; ++kt) tile(std::true_type{}, kt);
 
   // no direct-to-LDS load may still be writing when the workgroup's LDS is released
   wait_vmcnt_le<0>();
   const int any_bad = __syncthreads_or(local_bad);
   const float l_tot = l_run + shfl_xor_f32(l_run, 32);
   if (!row_ok) return;
-  const float inv = any_bad ? __builtin_nanf("") : 1.0f / l_tot;
-  __bf16* orow = out + ((int64_t)(c * a.chunk_len_max + qi) * a.num_q_heads + head) * D;
+  if constexpr (PREFIX) {
+    float* po = a.part_o + part_row * D;
 #pragma unroll
-  for (int nd = 0; nd < S::kND; ++nd)
+    for (int nd = 0; nd < S::kND; ++nd)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int dim = nd * 32 + 8 * q4 + 4 * half;
-      uint2 w;
-      w.x = pack_bf16x2(oacc[nd][4 * q4] * inv, oacc[nd][4 * q4 + 1] * inv);
-      w.y = pack_bf16x2(oacc[nd][4 * q4 + 2] * inv, oacc[nd][4 * q4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + dim) = w;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dim = nd * 32 + 8 * q4 + 4 * half;
+        *reinterpret_cast<float4*>(po + dim) =
+            make_float4(oacc[nd][4 * q4], oacc[nd][4 * q4 + 1], oacc[nd][4 * q4 + 2], oacc[nd][4 * q4 + 3]);
+      }
+    if (half == 0) {
+      a.part_ml[part_row * 2] = any_bad ? __builtin_nanf("") : m_run;
+      a.part_ml[part_row * 2 + 1] = l_tot;
     }
+  } else {
+    const float inv = any_bad ? __builtin_nanf("") : 1.0f / l_tot;
+    __bf16* orow = out + (out_row * a.num_q_heads + head) * D;
+#pragma unroll
+    for (int nd = 0; nd < S::kND; ++nd)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dim = nd * 32 + 8 * q4 + 4 * half;
+        uint2 w;
+        w.x = pack_bf16x2(oacc[nd][4 * q4] * inv, oacc[nd][4 * q4 + 1] * inv);
+        w.y = pack_bf16x2(oacc[nd][4 * q4 + 2] * inv, oacc[nd][4 * q4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dim) = w;
+      }
+  }
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
@@ -432,11 +478,33 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   switch (a.head_dim) {
     case 64:
-      hipLaunchKernelGGL(prefill_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+      hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
                          a.block_tables);
       break;
     case 128:
-      hipLaunchKernelGGL(prefill_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+      hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+                         a.block_tables);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_mfma(const PrefillArgs& a, hipStream_t stream) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (G < 1 || a.prefix_len <= 0 || a.split_tokens <= 0 || a.split_tokens % kKT != 0) return hipErrorInvalidValue;
+  const int64_t n_mt = ((int64_t)a.num_chunks * G + kMRows - 1) / kMRows;
+  const int64_t grid = n_mt * a.num_kv_heads * a.num_splits;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  switch (a.head_dim) {
+    case 64:
+      hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+                         a.block_tables);
+      break;
+    case 128:
+      hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
                          a.block_tables);
       break;
     default:

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == (1 << 16)
+    assert lib.pkv_abi_version() == (1 << 16) | 1
 
 
 def test_status_strings(lib):
@@ -133,3 +133,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pkv, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         pkv.load_library()
+
+
+def shared(lib, d, q=FAKE, B=2, hq=32, pb=FAKE, plen=64, maxb=4, ws=FAKE, wsb=1 << 30, scale=0.1):
+    return lib.paged_attn_decode_shared_prefix(q, B, hq, FAKE, FAKE, ctypes.byref(d), pb, plen, FAKE, maxb, FAKE,
+                                               scale, FAKE, ws, wsb, None)
+
+
+def test_shared_prefix_validation(lib):
+    d = desc()
+    assert shared(lib, d, B=0, q=None) == OK
+    assert shared(lib, d, q=None) == NULL
+    assert shared(lib, desc(dt=0)) == UNSUP        # float32: the prefix runs on the matrix cores
+    assert shared(lib, d, plen=40) == SHAPE        # not a multiple of 16
+    assert shared(lib, d, plen=-16) == SHAPE
+    assert shared(lib, d, pb=None) == NULL
+    assert shared(lib, d, hq=12) == SHAPE
+    assert shared(lib, d, scale=float("nan")) == SHAPE
+    need = lib.paged_attn_decode_shared_prefix_workspace_bytes(2, 32, 8, 128, 64)
+    assert need > lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 0)  # + the prefix partials
+    assert shared(lib, d, wsb=need - 1) == WS
+    assert shared(lib, d, ws=None) == WS
+    # no prefix: just the balanced decode's workspace
+    assert lib.paged_attn_decode_shared_prefix_workspace_bytes(2, 32, 8, 128, 0) == \
+        lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 0)

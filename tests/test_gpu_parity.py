@@ -334,3 +334,83 @@ def test_contract_violations_give_nan_not_faults(part):
     got = values(run_decode(dw, partition_tokens=part, max_context_len=128 * 16))
     assert np.isnan(got[0]).all() and np.isnan(got[1]).all() and np.isnan(got[2]).all()
     check_attn(got[3:], ref[3:], "bf16", "unaffected sequence")
+
+
+# ------------------------------------------------------------------ shared prefix (cascade)
+
+def run_shared_prefix(dw, w, n_pre):
+    """Decode through the shared-prefix entry: prefix = the first n_pre table entries."""
+    t = torch()
+    tab = w.block_tables
+    prefix = to_dev(np.ascontiguousarray(tab[0, :n_pre]).astype(np.int32), "bf16")
+    own = np.zeros((tab.shape[0], max(1, tab.shape[1] - n_pre)), dtype=np.int32)
+    own[:, :tab.shape[1] - n_pre] = tab[:, n_pre:]
+    own_lens = (w.context_lens - n_pre * 16).astype(np.int32)
+    out = empty_like_q(w.q.shape, w.dtype)
+    pkv.paged_attn_decode_shared_prefix(dw.q, dw.k_cache, dw.v_cache, prefix, to_dev(own, "bf16"),
+                                        to_dev(own_lens, "bf16"), float(w.scale), out)
+    t.cuda.synchronize()
+    return out, own, own_lens
+
+
+def test_shared_prefix_cfg4():
+    w = workloads.make(4)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    n_pre = len(w.shared_blocks)
+    assert (w.block_tables[:, :n_pre] == w.shared_blocks).all()
+    out, own, own_lens = run_shared_prefix(dw, w, n_pre)
+    ref = oracle.decode_shared_prefix(w.q, ref_k, ref_v, w.shared_blocks, own, own_lens, w.scale, w.dtype)
+    check_attn(values(out), ref, "bf16", "cascade cfg4")
+    # and the same as plain decode over the full tables
+    check_attn(values(out), values(run_decode(dw)), "bf16", "cascade vs plain decode")
+
+
+SHARED_CASES = [
+    # (hq, hkv, d, prefix_blocks, suffix lengths)
+    (32, 8, 128, 1, [1, 2, 15, 16, 17, 300]),
+    (32, 8, 128, 5, [0, 1, 700, 33] * 10),            # 80-token prefix (partial last tile), empty suffix
+    (64, 8, 128, 64, [1, 4000, 17, 2]),               # G = 8
+    (8, 8, 64, 3, [5, 100, 0, 64]),                   # G = 1, D = 64
+    (32, 8, 128, 128, [int(x) for x in np.random.default_rng(3).integers(1, 600, size=300)]),  # 300 seqs
+]
+
+
+@pytest.mark.parametrize("case", SHARED_CASES, ids=lambda c: f"{c[0]}q{c[1]}kv-d{c[2]}-p{c[3]}-b{len(c[4])}")
+def test_shared_prefix_parity(case):
+    hq, hkv, d, n_pre, suffix = case
+    rng = np.random.Generator(np.random.PCG64(31))
+    seqs = [SeqSpec(n_pre * 16 + n, n_new=1 if n else 0, shared_prefix=True) for n in suffix]
+    w = build(f"shared-{hq}-{d}-{n_pre}", 31, "bf16", hq, hkv, d, seqs, shared_prefix_blocks=n_pre, rng=rng)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    out, own, own_lens = run_shared_prefix(dw, w, n_pre)
+    ref = oracle.decode_shared_prefix(w.q, ref_k, ref_v, w.block_tables[0, :n_pre], own, own_lens, w.scale, w.dtype)
+    check_attn(values(out), ref, "bf16", f"cascade {case[:4]}")
+
+
+def test_shared_prefix_bad_blocks_give_nan():
+    rng = np.random.Generator(np.random.PCG64(32))
+    seqs = [SeqSpec(64 + n, shared_prefix=True) for n in (10, 20, 30)]
+    w = build("shared-bad", 32, "bf16", 32, 8, 128, seqs, shared_prefix_blocks=4, rng=rng)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    t = torch()
+    own = np.ascontiguousarray(w.block_tables[:, 4:]).astype(np.int32)
+    own_lens = (w.context_lens - 64).astype(np.int32)
+    own_bad = own.copy()
+    own_bad[1, 0] = w.num_blocks + 5  # sequence 1's own block out of the pool
+    out = empty_like_q(w.q.shape, w.dtype)
+    pkv.paged_attn_decode_shared_prefix(dw.q, dw.k_cache, dw.v_cache, to_dev(w.block_tables[0, :4].copy(), "bf16"),
+                                        to_dev(own_bad, "bf16"), to_dev(own_lens, "bf16"), float(w.scale), out)
+    t.cuda.synchronize()
+    got = values(out)
+    ref = oracle.decode_shared_prefix(w.q, ref_k, ref_v, w.block_tables[0, :4], own, own_lens, w.scale, w.dtype)
+    assert np.isnan(got[1]).all()
+    check_attn(got[[0, 2]], ref[[0, 2]], "bf16", "unaffected sequences")
+    prefix_bad = w.block_tables[0, :4].copy()
+    prefix_bad[2] = -3  # a prefix block out of range: every output NaN
+    pkv.paged_attn_decode_shared_prefix(dw.q, dw.k_cache, dw.v_cache, to_dev(prefix_bad, "bf16"),
+                                        to_dev(own, "bf16"), to_dev(own_lens, "bf16"), float(w.scale), out)
+    t.cuda.synchronize()
+    assert np.isnan(values(out)).all()

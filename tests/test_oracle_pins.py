@@ -323,3 +323,30 @@ def test_bf16_widening_is_exact():
     bits = np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x4049], np.uint16)
     ref = [1.0, -1.0, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, 3.140625]
     assert list(oracle.to_f64(bits, "bf16")) == ref
+
+
+def test_shared_prefix_decode_brute_force():
+    """Shared-prefix decode against a per-sequence recompute over the concatenated
+    context (prefix tokens, then the sequence's own), from contiguous lists."""
+    rng = np.random.default_rng(21)
+    hkv, G, d, pre = 2, 2, 8, 32
+    suffix = [0, 5, 17, 40]
+    base_k, base_v = rand(rng, pre, hkv, d), rand(rng, pre, hkv, d)
+    own_k = [rand(rng, n, hkv, d) for n in suffix]
+    own_v = [rand(rng, n, hkv, d) for n in suffix]
+    q = rand(rng, len(suffix), hkv * G, d)
+    # the pool: prefix blocks once, then each sequence's own blocks
+    full_k = [np.concatenate([base_k, k]) for k in own_k]
+    full_v = [np.concatenate([base_v, v]) for v in own_v]
+    kc, vc, tab, lens = place(full_k, full_v, 24, rng, shared=pre)
+    prefix_blocks = tab[0, :pre // 16].copy()
+    own_tables = np.zeros((len(suffix), tab.shape[1]), dtype=np.int32)
+    own_tables[:, :tab.shape[1] - pre // 16] = tab[:, pre // 16:]
+    got = oracle.decode_shared_prefix(q, kc, vc, prefix_blocks, own_tables, np.array(suffix), 0.35, "f32")
+    for s in range(len(suffix)):
+        for h in range(hkv * G):
+            g = h // G
+            keys = [list(map(float, full_k[s][t, g])) for t in range(pre + suffix[s])]
+            vals = [list(map(float, full_v[s][t, g])) for t in range(pre + suffix[s])]
+            ref = bruteforce.attend_one(list(map(float, q[s, h])), keys, vals, oracle.exact_scale(0.35))
+            np.testing.assert_allclose(got[s, h], ref, rtol=1e-12, atol=1e-13)

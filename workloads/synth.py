@@ -197,7 +197,7 @@ def build(
     for s, n in zip(seqs, nblk):
         if s.shared_prefix:
             assert n >= sp and s.length - s.n_new >= sp * bs, "writes must not touch shared blocks"
-        assert 0 < s.n_new <= s.length or (s.length == 0 and s.n_new == 0)
+        assert 0 <= s.n_new <= s.length
     private = sum(n - (sp if s.shared_prefix else 0) for s, n in zip(seqs, nblk))
     total = private + sp
     if num_blocks is None:
