@@ -74,6 +74,8 @@ def parse():
     p.add_argument("--partition", type=int, default=0,
                    help="decode partition tokens (0 = balanced split over a fixed number of wavefronts)")
     p.add_argument("--cold", action="store_true", help="overwrite 512 MB before every step (LLC-cold timing)")
+    p.add_argument("--no-cascade", action="store_true",
+                   help="shared-prefix workload: plain decode over the full tables instead of the shared-prefix call")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     p.add_argument("--copy-probe-mb", type=int, default=0,
@@ -118,8 +120,18 @@ def main():
                                       to_dev(w.chunk_context_lens))
         oc = torch.empty_like(qc)
     part = args.partition  # 0: balanced split
-    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                          w.max_context_len, part)
+    cascade = w.shared_blocks is not None and not args.no_cascade and part == 0
+    if cascade:  # the shared prefix once, then each sequence's own blocks
+        n_pre = len(w.shared_blocks)
+        assert (w.block_tables[:, :n_pre] == w.shared_blocks).all()
+        prefix = to_dev(w.shared_blocks.astype(np.int32))
+        own_tables = to_dev(np.ascontiguousarray(w.block_tables[:, n_pre:]).astype(np.int32))
+        own_lens = to_dev((w.context_lens - n_pre * 16).astype(np.int32))
+        ws_bytes = pkv.shared_prefix_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                                     n_pre * 16)
+    else:
+        ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                              w.max_context_len, part)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if args.cold else None
     scale = float(w.scale)
@@ -128,8 +140,11 @@ def main():
         pkv.paged_kv_write(nk, nv, slots, kc, vc)
 
     def decode():
-        pkv.paged_attn_decode(q, kc, vc, tables, lens, scale, out, max_context_len=w.max_context_len,
-                              partition_tokens=part, workspace=ws)
+        if cascade:
+            pkv.paged_attn_decode_shared_prefix(q, kc, vc, prefix, own_tables, own_lens, scale, out, workspace=ws)
+        else:
+            pkv.paged_attn_decode(q, kc, vc, tables, lens, scale, out, max_context_len=w.max_context_len,
+                                  partition_tokens=part, workspace=ws)
 
     def prefill():
         pkv.paged_attn_prefill_chunk(qc, cstart, kc, vc, ctables, clens, scale, oc)
@@ -195,8 +210,10 @@ def main():
         traffic = tr["read_bytes"] + tr["write_bytes"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "paged_attn_decode: decode_balanced_kernel + decode_balanced_merge_kernel"
-                          if part == 0 else "paged_attn_decode: decode_partition_kernel + decode_merge_kernel",
+                "kernel": ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
+                           "decode_balanced_kernel + decode_balanced_merge_kernel") if cascade else
+                          ("paged_attn_decode: decode_balanced_kernel + decode_balanced_merge_kernel"
+                           if part == 0 else "paged_attn_decode: decode_partition_kernel + decode_merge_kernel"),
                 "algorithmic_bytes_per_launch": dec["total"], "launch_ms_mean": round(dec_ms, 5),
                 "traffic_read_write_bytes": [tr["read_bytes"], tr["write_bytes"]] if traffic else None}
 
@@ -209,6 +226,8 @@ def main():
                    "block_size": 16, "num_blocks": w.num_blocks, "context_tokens": int(w.context_lens.sum()),
                    "max_context_len": w.max_context_len,
                    "split": f"fixed partitions of {part} tokens" if part else
+                            (f"shared prefix of {len(w.shared_blocks) * 16} tokens attended once, then " if cascade
+                             else "") +
                             f"balanced over {pkv.decode_split_waves(w.num_q_heads, w.num_kv_heads)} wavefronts",
                    "kv_bytes_per_step": kv_bytes, "llc": "cold (512 MB overwrite per step)" if args.cold else "warm",
                    "layers_per_step": 1},

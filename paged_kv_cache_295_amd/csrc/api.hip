@@ -219,6 +219,10 @@ int paged_attn_decode_shared_prefix(const void* q, int32_t num_seqs, int32_t num
     pa.part_ml = pre_ml;
     st = from_hip(launch_prefix_mfma(pa, as_stream(hip_stream)));
     if (st != PKV_OK) return st;
+    // one partial per (sequence, head): every stream then starts from a single load
+    st = from_hip(launch_prefix_merge(pre_o, pre_ml, (int64_t)num_seqs * num_q_heads, ps.splits, cache->head_dim,
+                                      as_stream(hip_stream)));
+    if (st != PKV_OK) return st;
   }
   DecodeArgs a{};
   a.q = q;
@@ -246,7 +250,7 @@ int paged_attn_decode_shared_prefix(const void* q, int32_t num_seqs, int32_t num
   if (prefix_len > 0) {
     a.init_o = pre_o;
     a.init_ml = pre_o + (size_t)ps.splits * num_seqs * num_q_heads * cache->head_dim;
-    a.init_splits = ps.splits;
+    a.init_splits = 1;  // merged above
   }
   return from_hip(launch_decode(a, as_stream(hip_stream)));
 }

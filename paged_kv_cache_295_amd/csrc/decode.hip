@@ -816,6 +816,57 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
   }
 }
 
+// Shared prefix: merge the `splits` partials of every (sequence, head) row
+// into the first one, in place (max M, sum sum_p 2^{m_p - M} l_p, output
+// sum_p 2^{m_p - M} o_p), so that a stream starts from one partial.  One wave
+// per row; lane k owns dims k, k + 64, ...
+template <int D>
+__global__ __launch_bounds__(64) void prefix_merge_kernel(float* __restrict__ part_o, float* __restrict__ part_ml,
+                                                          int64_t rows, int splits) {
+  constexpr int PER = D / kWave;
+  const int lane = __lane_id();
+  const int64_t row = blockIdx.x;
+  if (row >= rows) return;
+  float M = -__builtin_inff();
+  bool nan = false;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float m = part_ml[(sp * rows + row) * 2];
+    nan |= m != m;
+    M = fmaxf(M, m);
+  }
+  float lam = 0.0f, o[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const int64_t r = sp * rows + row;
+    const float f = fast_exp2(part_ml[r * 2] - M);
+    lam = fmaf(f, part_ml[r * 2 + 1], lam);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = fmaf(f, part_o[r * D + lane + e * kWave], o[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) part_o[row * D + lane + e * kWave] = o[e];
+  if (lane == 0) {
+    part_ml[row * 2] = nan ? __builtin_nanf("") : M;
+    part_ml[row * 2 + 1] = lam;
+  }
+}
+
+hipError_t launch_prefix_merge(float* part_o, float* part_ml, int64_t rows, int splits, int head_dim,
+                               hipStream_t stream) {
+  if (rows <= 0 || splits <= 1) return hipSuccess;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(prefix_merge_kernel<64>, dim3((unsigned)rows), dim3(64), 0, stream, part_o, part_ml, rows,
+                       splits);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(prefix_merge_kernel<128>, dim3((unsigned)rows), dim3(64), 0, stream, part_o, part_ml, rows,
+                       splits);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // Lanes per token: fewer lanes per token means fewer DPP reduction steps and
 // less redundant softmax work per block, at the price of more accumulator
 // registers per lane (head_dim / LPT floats per head).  8 for up to four heads

@@ -91,6 +91,9 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefix_mfma(const PrefillArgs& a, hipStream_t stream);
+// Merges the splits partials of each of `rows` rows into the first split's slot.
+hipError_t launch_prefix_merge(float* part_o, float* part_ml, int64_t rows, int splits, int head_dim,
+                               hipStream_t stream);
 
 // Heads processed together by one wave for a GQA group of size g.
 constexpr int heads_per_wave(int g) {
