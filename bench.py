@@ -62,6 +62,7 @@ WORKLOADS = {
     "mixed-step": 3,
     "shared-prefix": 4,
     "long-context": 5,
+    "spec-verify": "spec-verify",  # supplementary: speculative-decoding verify (5-row chunks)
 }
 
 
@@ -78,6 +79,8 @@ def parse():
                    help="shared-prefix workload: plain decode over the full tables instead of the shared-prefix call")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    p.add_argument("--copy-pairs", type=int, default=512,
+                   help="block pairs of the supplementary copy-on-write measurement (0: skip)")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="after timing, run one device copy of this many MiB (calibrates HBM byte counters)")
     return p.parse_args()
@@ -198,34 +201,46 @@ def main():
         ms_per_step = max(ms_per_step - flush_ms, 1e-6)
 
     eb = w.elem_bytes
-    dec = accounting.decode_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
-                                  block_tables=w.block_tables, dedupe_shared=(cfg == 4))
-    kv_bytes = dec["kv"]
+    verify = w.num_seqs == 0 and has_chunks  # the verify pass: chunk rows only
+    if verify:
+        pb = accounting.prefill_bytes(w.chunk_start, w.chunk_context_lens, w.num_q_heads, w.num_kv_heads,
+                                      w.head_dim, eb)
+        kv_bytes = int(w.chunk_context_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 2 * eb
+        dec = {"kv": kv_bytes, "total": pb}
+        n_seq, launch_ms = w.num_chunks, pre_ms
+    else:
+        dec = accounting.decode_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
+                                      block_tables=w.block_tables, dedupe_shared=(cfg == 4))
+        kv_bytes = dec["kv"]
+        n_seq, launch_ms = w.num_seqs, dec_ms
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    seq_tok_s = w.num_seqs / (ms_per_step * 1e-3)
-    achieved = dec["total"] / (dec_ms * 1e-3) / 1e9 if dec_ms > 0 else 0.0
+    seq_tok_s = n_seq / (ms_per_step * 1e-3)
+    achieved = dec["total"] / (launch_ms * 1e-3) / 1e9 if launch_ms > 0 else 0.0
     tr = TRAFFIC.get(w.name)
     traffic = None
     if tr is not None and tr["sources_sha256"] == sources_sha256() and part == 0 and not args.cold:
         traffic = tr["read_bytes"] + tr["write_bytes"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
+                "kernel": "paged_attn_prefill_chunk: prefill_mfma_kernel" if verify else
+                          ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
                            "decode_balanced_kernel + decode_balanced_merge_kernel") if cascade else
                           ("paged_attn_decode: decode_balanced_kernel + decode_balanced_merge_kernel"
                            if part == 0 else "paged_attn_decode: decode_partition_kernel + decode_merge_kernel"),
-                "algorithmic_bytes_per_launch": dec["total"], "launch_ms_mean": round(dec_ms, 5),
+                "algorithmic_bytes_per_launch": dec["total"], "launch_ms_mean": round(launch_ms, 5),
                 "traffic_read_write_bytes": [tr["read_bytes"], tr["write_bytes"]] if traffic else None}
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "description": w.description, "seed": w.seed, "num_seqs": w.num_seqs,
+        "config": {"workload": w.name, "description": w.description, "seed": w.seed, "num_seqs": n_seq,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "block_size": 16, "num_blocks": w.num_blocks, "context_tokens": int(w.context_lens.sum()),
+                   "block_size": 16, "num_blocks": w.num_blocks,
+                   "context_tokens": int((w.chunk_context_lens if verify else w.context_lens).sum()),
                    "max_context_len": w.max_context_len,
-                   "split": f"fixed partitions of {part} tokens" if part else
+                   "split": "one workgroup per (chunk, kv head)" if verify else
+                            f"fixed partitions of {part} tokens" if part else
                             (f"shared prefix of {len(w.shared_blocks) * 16} tokens attended once, then " if cascade
                              else "") +
                             f"balanced over {pkv.decode_split_waves(w.num_q_heads, w.num_kv_heads)} wavefronts",
@@ -244,6 +259,19 @@ def main():
                           "tflops": round(flops / (pm * 1e-3) / 1e12, 2),
                           "mfma_frac_of_bf16_peak": round(flops / (pm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
+    if args.copy_pairs and not verify:
+        # supplementary: copy-on-write block copies, cached blocks into blocks no table holds
+        held = set(np.asarray(w.block_tables).ravel().tolist()) | set(np.asarray(w.chunk_tables).ravel().tolist())
+        free = np.array([b for b in range(w.num_blocks) if b not in held], dtype=np.int32)
+        n_pairs = min(args.copy_pairs, len(free))
+        rng = np.random.default_rng(w.seed)
+        src_blocks = to_dev(rng.choice(np.array(sorted(held), dtype=np.int32), n_pairs, replace=False))
+        dst_blocks = to_dev(free[:n_pairs])
+        copy_ms = timed(lambda: pkv.paged_kv_copy_blocks(src_blocks, dst_blocks, kc, vc), K)
+        cb = accounting.copy_bytes(n_pairs, w.num_kv_heads, w.head_dim, eb)
+        res["copy_blocks"] = {"pairs": n_pairs, "algorithmic_bytes": cb, "ms_mean": round(copy_ms, 5),
+                              "gbs": round(cb / (copy_ms * 1e-3) / 1e9, 1),
+                              "frac_of_hbm_peak": round(cb / (copy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if args.copy_probe_mb:
         n = args.copy_probe_mb * 1024 * 1024 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -258,35 +286,41 @@ def main():
 
 
 def cpu_baseline(w, seconds, cfg):
-    """The fp64 oracle (write + decode of the same step) timed on one host thread."""
-    import numpy as np
+    """The fp64 oracle (write + attention of the same step) timed on one host thread."""
     from threadpoolctl import threadpool_limits
 
     import oracle
-    from workloads import accounting
 
-    # sample: whole sequences of the batch, in order, until ~`seconds` of CPU work
-    done_seqs, done_tokens, t_total, reps = 0, 0, 0.0, 0
+    # sample: whole sequences (decode) or chunks (verify rows) of the batch, in
+    # order, until ~`seconds` of CPU work
+    verify = w.num_seqs == 0
+    n_items = w.num_chunks if verify else w.num_seqs
+    lens = w.chunk_context_lens if verify else w.context_lens
+    done_seqs, done_tokens, t_total = 0, 0, 0.0
     with threadpool_limits(1):
         t0 = time.perf_counter()
         rk, rv = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
         t_total += time.perf_counter() - t0
-        while t_total < seconds:
-            for s in range(w.num_seqs):
+        while n_items and t_total < seconds:
+            for s in range(n_items):
                 t0 = time.perf_counter()
-                oracle.decode(w.q[s:s + 1], rk, rv, w.block_tables[s:s + 1], w.context_lens[s:s + 1], w.scale,
-                              w.dtype)
+                if verify:
+                    oracle.prefill_chunk(w.q_chunk[s:s + 1], w.chunk_start[s:s + 1], rk, rv, w.chunk_tables[s:s + 1],
+                                         w.chunk_context_lens[s:s + 1], w.scale, w.dtype)
+                else:
+                    oracle.decode(w.q[s:s + 1], rk, rv, w.block_tables[s:s + 1], w.context_lens[s:s + 1], w.scale,
+                                  w.dtype)
                 t_total += time.perf_counter() - t0
                 done_seqs += 1
-                done_tokens += int(w.context_lens[s])
+                done_tokens += int(lens[s])
                 if t_total >= seconds:
                     break
-            reps += 1
     row = w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
+    what = "verify chunks" if verify else "decode"
     return {"value": round(done_tokens * row / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seq_tokens_per_s": round(done_seqs / t_total, 2),
-            "sample": f"fp64 numpy oracle, one thread: cache write of the step's {len(w.slot_mapping)} rows + decode "
-                      f"of {done_seqs} sequences taken in batch order ({done_tokens} context tokens), "
+            "sample": f"fp64 numpy oracle, one thread: cache write of the step's {len(w.slot_mapping)} rows + "
+                      f"{what} of {done_seqs} sequences taken in batch order ({done_tokens} context tokens), "
                       f"{t_total:.1f} s"}
 
 

@@ -59,6 +59,7 @@ extern "C" {
 #define PKV_ERR_UNSUPPORTED (-4) /* block_size != 16, or head_dim not 64 or 128 */
 #define PKV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than the query function requires */
 #define PKV_ERR_HIP (-6)         /* a kernel launch failed (hipGetLastError after launch) */
+#define PKV_ERR_NO_BLOCKS (-7)   /* block bookkeeping: the free pool is empty */
 
 #define PKV_DTYPE_F32 0
 #define PKV_DTYPE_BF16 1
@@ -90,6 +91,62 @@ typedef struct pkv_cache_desc {
  */
 int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int64_t num_tokens,
                    void* k_cache, void* v_cache, const pkv_cache_desc* cache, void* hip_stream);
+
+/*
+ * paged_kv_copy_blocks -- copy whole cache blocks: for each i,
+ * block dst_blocks[i] of k_cache and of v_cache (every kv head, all 16 slots)
+ * becomes a copy of block src_blocks[i].  (ainews.alishangtian.com article,
+ * section "PagedAttention": a block shared by several sequences is copied to
+ * a block of its own before one of them writes into it -- copy-on-write.)
+ *
+ *   src_blocks, dst_blocks   int32 [num_pairs] (device)
+ *
+ * A raw copy of the bit patterns (bit-exact).  A pair with an id outside
+ * [0, num_blocks) is skipped, src == dst is a no-op; a block that is the
+ * destination of one pair and the source or destination of another in the same
+ * call gets an unspecified one of the candidate contents.  num_pairs == 0 is a
+ * no-op that returns PKV_OK.
+ */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* cache, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int64_t num_pairs, void* hip_stream);
+
+/*
+ * Host-side block bookkeeping for copy-on-write sharing (same "PagedAttention"
+ * section of the inference-engine article on ainews.alishangtian.com).  Plain
+ * host memory, no GPU work, not thread-safe; every array is owned by the
+ * caller:
+ *
+ *   ref_counts   int32 [num_blocks]  how many block tables hold each block
+ *   free_list    int32 [num_blocks]  a stack of unheld blocks, the first
+ *                                    *free_count entries valid; pops take the last
+ *   tables       int32 [max_blocks_per_seq] per sequence, as for the attention calls
+ *
+ * paged_block_fork: child_table[0 .. num_table_blocks) = parent_table[...], and
+ *   each of those blocks gains a holder.  Nothing is copied: the child shares
+ *   every block, the partially filled last one included.
+ * paged_block_append_slot: the slot for a sequence's next token, at position
+ *   context_len (the tokens it already has).  A token at offset 0 of a block
+ *   takes a block from the free list.  A token inside a block that other
+ *   sequences also hold first moves this sequence to a copy: a free block
+ *   replaces the shared one in `table`, the shared one loses a holder, and
+ *   (*copy_src, *copy_dst) is the pair to pass to paged_kv_copy_blocks before
+ *   the token is written (*num_copies = 1; else 0).  *slot = block * 16 + offset.
+ * paged_block_release: each of the table's blocks loses a holder; a block left
+ *   with none goes back on the free list.  A table must not hold a block twice.
+ *
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (a count out of range, a block id outside
+ * [0, num_blocks), a held block whose count is below one, a free block whose
+ * count is not zero, a position beyond max_blocks_per_seq * 16, a duplicate in
+ * a released table), PKV_ERR_NO_BLOCKS (free list empty).  On any error
+ * nothing has been changed.
+ */
+int paged_block_fork(const int32_t* parent_table, int32_t num_table_blocks, int32_t* child_table,
+                     int32_t* ref_counts, int32_t num_blocks);
+int paged_block_append_slot(int32_t* table, int32_t max_blocks_per_seq, int32_t context_len, int32_t* ref_counts,
+                            int32_t num_blocks, int32_t* free_list, int32_t* free_count, int32_t* slot,
+                            int32_t* copy_src, int32_t* copy_dst, int32_t* num_copies);
+int paged_block_release(const int32_t* table, int32_t num_table_blocks, int32_t* ref_counts, int32_t num_blocks,
+                        int32_t* free_list, int32_t* free_count);
 
 /*
  * Split-context decode.  A sequence's context is cut into pieces; each piece
@@ -215,7 +272,7 @@ const char* pkv_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION ((1 << 16) | 1)
+#define PKV_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

@@ -101,6 +101,25 @@ def kv_write(k_cache, v_cache, new_k, new_v, slot_mapping):
 
 # ---------------------------------------------------------------- gather
 
+def copy_blocks(k_cache, v_cache, src_blocks, dst_blocks):
+    """Copy-on-write of whole blocks.
+
+    ainews.alishangtian.com article on inference engines, section
+    "PagedAttention": a physical block shared by several sequences is copied
+    to a block of its own before one of them modifies it.  Returns new caches
+    in which block dst[i] holds the bits of block src[i] (every kv head, all
+    slots); pairs naming an id outside [0, num_blocks) are skipped.  Raw bits
+    are copied, so NaN payloads survive.
+    """
+    kc, vc = k_cache.copy(), v_cache.copy()
+    nb = k_cache.shape[0]
+    for s, d in zip(np.asarray(src_blocks).tolist(), np.asarray(dst_blocks).tolist()):
+        if 0 <= s < nb and 0 <= d < nb:
+            kc[d] = k_cache[s]
+            vc[d] = v_cache[s]
+    return kc, vc
+
+
 def gather(cache, table_row, length: int) -> np.ndarray:
     """Contiguous [length, kv_heads, head_dim] copy (raw) of a sequence's cached rows."""
     out = np.empty((length,) + cache.shape[1:2] + cache.shape[3:], dtype=cache.dtype)

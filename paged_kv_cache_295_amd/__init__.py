@@ -16,7 +16,7 @@ import os
 __all__ = [
     "PagedKVError", "load_library", "paged_kv_write", "paged_attn_decode", "paged_attn_prefill_chunk",
     "decode_workspace_bytes", "decode_split_waves", "library_path", "BLOCK_SIZE",
-    "paged_attn_decode_shared_prefix", "shared_prefix_workspace_bytes",
+    "paged_attn_decode_shared_prefix", "shared_prefix_workspace_bytes", "paged_kv_copy_blocks", "BlockPool",
 ]
 
 BLOCK_SIZE = 16
@@ -57,6 +57,8 @@ def load_library():
     cdp = ctypes.POINTER(CacheDesc)
     lib.paged_kv_write.argtypes = [vp, vp, vp, i64, vp, vp, cdp, vp]
     lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_kv_copy_blocks.argtypes = [vp, vp, cdp, vp, vp, i64, vp]
+    lib.paged_kv_copy_blocks.restype = ctypes.c_int
     lib.paged_attn_decode_split_waves.argtypes = [i32, i32]
     lib.paged_attn_decode_split_waves.restype = i32
     lib.paged_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -70,6 +72,13 @@ def load_library():
     lib.paged_attn_decode_shared_prefix.restype = ctypes.c_int
     lib.paged_attn_prefill_chunk.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp]
     lib.paged_attn_prefill_chunk.restype = ctypes.c_int
+    ip = ctypes.POINTER(i32)
+    lib.paged_block_fork.argtypes = [ip, i32, ip, ip, i32]
+    lib.paged_block_fork.restype = ctypes.c_int
+    lib.paged_block_append_slot.argtypes = [ip, i32, i32, ip, i32, ip, ip, ip, ip, ip, ip]
+    lib.paged_block_append_slot.restype = ctypes.c_int
+    lib.paged_block_release.argtypes = [ip, i32, ip, i32, ip, ip]
+    lib.paged_block_release.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -142,6 +151,20 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
     st = lib.paged_kv_write(_ptr(k), _ptr(v), _i32(slot_mapping, "slot_mapping"), k.shape[0], _ptr(k_cache),
                             _ptr(v_cache), ctypes.byref(desc), _stream(stream))
     _check(st, "paged_kv_write")
+
+
+def paged_kv_copy_blocks(src_blocks, dst_blocks, k_cache, v_cache, stream=None):
+    """Copy block src_blocks[i] to block dst_blocks[i] in both caches (int32 [N] each)."""
+    lib = load_library()
+    _same_dtype(k_cache, v_cache)
+    desc = _cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if src_blocks.dim() != 1 or dst_blocks.shape != src_blocks.shape:
+        raise ValueError("src_blocks and dst_blocks must be [N]")
+    st = lib.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _i32(src_blocks, "src_blocks"),
+                                  _i32(dst_blocks, "dst_blocks"), src_blocks.shape[0], _stream(stream))
+    _check(st, "paged_kv_copy_blocks")
 
 
 def decode_split_waves(num_q_heads: int, num_kv_heads: int) -> int:
@@ -240,3 +263,57 @@ def paged_attn_prefill_chunk(q_chunk, chunk_start, k_cache, v_cache, block_table
                                       _stream(stream))
     _check(st, "paged_attn_prefill_chunk")
     return out
+
+
+class BlockPool:
+    """Host block bookkeeping for copy-on-write sharing (paged_block_* calls).
+
+    Holds the per-block holder counts and the free-list stack as int32 numpy
+    arrays; block tables are int32 numpy arrays the caller owns.  All decisions
+    are the library's; this class only passes the arrays.
+    """
+
+    def __init__(self, num_blocks: int):
+        import numpy as np
+        self.num_blocks = int(num_blocks)
+        self.ref_counts = np.zeros(self.num_blocks, dtype=np.int32)
+        # popped from the end: block 0 first
+        self.free_list = np.arange(self.num_blocks - 1, -1, -1, dtype=np.int32)
+        self._free_count = ctypes.c_int32(self.num_blocks)
+
+    @property
+    def free_count(self) -> int:
+        return int(self._free_count.value)
+
+    @staticmethod
+    def _p(a, name):
+        import numpy as np
+        if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous):
+            raise TypeError(f"{name} must be a contiguous int32 numpy array")
+        return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def fork(self, parent_table, num_table_blocks: int, child_table):
+        """child_table[:n] = parent_table[:n]; each shared block gains a holder."""
+        lib = load_library()
+        _check(lib.paged_block_fork(self._p(parent_table, "parent_table"), int(num_table_blocks),
+                                    self._p(child_table, "child_table"), self._p(self.ref_counts, "ref_counts"),
+                                    self.num_blocks), "paged_block_fork")
+
+    def append_slot(self, table, context_len: int):
+        """Slot of the token at position context_len; (src, dst) block copy to run first, or None."""
+        lib = load_library()
+        slot, src, dst, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.paged_block_append_slot(self._p(table, "table"), int(table.shape[-1]), int(context_len),
+                                           self._p(self.ref_counts, "ref_counts"), self.num_blocks,
+                                           self._p(self.free_list, "free_list"), ctypes.byref(self._free_count),
+                                           ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst), ctypes.byref(n)),
+               "paged_block_append_slot")
+        return int(slot.value), ((int(src.value), int(dst.value)) if n.value else None)
+
+    def release(self, table, num_table_blocks: int):
+        """Each of the table's first num_table_blocks blocks loses a holder; unheld blocks are freed."""
+        lib = load_library()
+        _check(lib.paged_block_release(self._p(table, "table"), int(num_table_blocks),
+                                       self._p(self.ref_counts, "ref_counts"), self.num_blocks,
+                                       self._p(self.free_list, "free_list"), ctypes.byref(self._free_count)),
+               "paged_block_release")

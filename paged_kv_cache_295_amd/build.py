@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "block_table.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 ops are kept out of the device code (v_pk_fma_f32 and friends).

@@ -83,6 +83,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported block size or head dim";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch error";
+    case PKV_ERR_NO_BLOCKS: return "no free cache block";
   }
   return "unknown status";
 }
@@ -97,6 +98,19 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
   WriteArgs a{k, v, slot_mapping, num_tokens, k_cache, v_cache, cache->num_blocks, cache->num_kv_heads,
               cache->head_dim, cache->dtype};
   return from_hip(launch_kv_write(a, as_stream(hip_stream)));
+}
+
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* cache, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int64_t num_pairs, void* hip_stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks) return PKV_ERR_NULL;
+  const int64_t elem = cache->dtype == PKV_DTYPE_BF16 ? 2 : 4;
+  const int64_t block_bytes = (int64_t)cache->num_kv_heads * PKV_BLOCK_SIZE * cache->head_dim * elem;
+  return from_hip(launch_kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, num_pairs, cache->num_blocks,
+                                        block_bytes, as_stream(hip_stream)));
 }
 
 int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads) {

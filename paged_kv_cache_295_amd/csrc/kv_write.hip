@@ -66,4 +66,40 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Copy-on-write: copy whole blocks (every kv head, all 16 slots, K and V).
+// ainews.alishangtian.com article on inference engines, section
+// "PagedAttention": sequences share physical blocks, and a shared block that
+// one of them must modify is first copied to a block of its own.  One
+// workgroup per (src, dst) pair, 16-byte copies; pairs with an id outside
+// [0, num_blocks) are skipped.
+__global__ __launch_bounds__(256) void kv_copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                                             const int32_t* __restrict__ src_blocks,
+                                                             const int32_t* __restrict__ dst_blocks,
+                                                             int64_t num_pairs, int32_t num_blocks,
+                                                             int64_t block_chunks) {
+  for (int64_t i = blockIdx.x; i < num_pairs; i += gridDim.x) {
+    const int32_t src = src_blocks[i], dst = dst_blocks[i];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) continue;
+    const uint4* ks = k_cache + (int64_t)src * block_chunks;
+    const uint4* vs = v_cache + (int64_t)src * block_chunks;
+    uint4* kd = k_cache + (int64_t)dst * block_chunks;
+    uint4* vd = v_cache + (int64_t)dst * block_chunks;
+    for (int64_t j = threadIdx.x; j < block_chunks; j += blockDim.x) {
+      const uint4 a = ks[j];
+      const uint4 b = vs[j];
+      kd[j] = a;
+      vd[j] = b;
+    }
+  }
+}
+
+hipError_t launch_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                                 int64_t num_pairs, int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+  const int64_t grid64 = num_pairs < 65536 ? num_pairs : 65536;
+  hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3((unsigned)grid64), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), src, dst, num_pairs,
+                     num_blocks, block_bytes / 16);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -87,6 +87,8 @@ struct PrefillArgs {
 };
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                                 int64_t num_pairs, int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
 // Returns hipErrorInvalidValue if no instantiation covers the shape.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);

@@ -39,11 +39,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == (1 << 16) | 1
+    assert lib.pkv_abi_version() == (1 << 16) | 2
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, DTYPE, SHAPE, UNSUP, WS, -6):
+    for code in (OK, NULL, DTYPE, SHAPE, UNSUP, WS, -6, -7):
         s = lib.pkv_status_string(code)
         assert s and s != b"unknown status"
     assert lib.pkv_status_string(42) == b"unknown status"
@@ -157,3 +157,13 @@ def test_shared_prefix_validation(lib):
     # no prefix: just the balanced decode's workspace
     assert lib.paged_attn_decode_shared_prefix_workspace_bytes(2, 32, 8, 128, 0) == \
         lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 0)
+
+
+def test_copy_blocks_validation(lib):
+    d = desc()
+    assert lib.paged_kv_copy_blocks(FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, 0, None) == OK
+    assert lib.paged_kv_copy_blocks(FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, -1, None) == SHAPE
+    assert lib.paged_kv_copy_blocks(None, FAKE, ctypes.byref(d), FAKE, FAKE, 3, None) == NULL
+    assert lib.paged_kv_copy_blocks(FAKE, FAKE, ctypes.byref(d), None, FAKE, 3, None) == NULL
+    assert lib.paged_kv_copy_blocks(FAKE, FAKE, None, FAKE, FAKE, 3, None) == NULL
+    assert lib.paged_kv_copy_blocks(FAKE, FAKE, ctypes.byref(desc(dt=5)), FAKE, FAKE, 3, None) == DTYPE

@@ -269,6 +269,30 @@ def test_prefill_chunk_parity(case):
     write_decode_prefill_vs_oracle(w, f"prefill {case}")
 
 
+# speculative-decoding verify: many sequences with k + 1 = 2..9 causal rows each
+VERIFY_CASES = [
+    ("bf16", 32, 8, 128, 5, 40, 11),
+    ("bf16", 64, 8, 128, 3, 24, 12),
+    ("bf16", 32, 8, 128, 9, 16, 13),
+    ("bf16", 8, 8, 64, 2, 30, 14),
+    ("f32", 32, 8, 128, 5, 12, 15),
+]
+
+
+@pytest.mark.parametrize("case", VERIFY_CASES, ids=lambda c: f"{c[0]}-{c[1]}q{c[2]}kv-{c[3]}d-rows{c[4]}-{c[5]}seqs")
+def test_spec_verify_parity(case):
+    """Each sequence verifies up to k drafts: a chunk of 1..k+1 rows (ragged: some
+    sequences accepted fewer) over contexts from a few tokens to a few thousand."""
+    dtype, hq, hkv, d, rows, nseq, seed = case
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(1, 3000, size=nseq)
+    ctx[:3] = [0, 15, 16]  # empty context, a ragged block, an exact block
+    n = rng.integers(1, rows + 1, size=nseq)
+    n[:2] = rows
+    w = chunk_workload(dtype, hq, hkv, d, list(zip(ctx.tolist(), n.tolist())), seed=seed, cmax=rows)
+    write_decode_prefill_vs_oracle(w, f"verify {case}")
+
+
 def test_prefill_last_row_equals_decode():
     """The last row of a chunk is the decode query of the same position."""
     w = chunk_workload("bf16", 32, 8, 128, [(300, 200)], seed=12)
@@ -414,3 +438,114 @@ def test_shared_prefix_bad_blocks_give_nan():
                                         to_dev(own, "bf16"), to_dev(own_lens, "bf16"), float(w.scale), out)
     t.cuda.synchronize()
     assert np.isnan(values(out)).all()
+
+
+# ------------------------------------------------------------------ copy-on-write block copy
+
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f32", 8, 64), ("bf16", 2, 64)])
+def test_copy_blocks_bit_exact(dtype, hkv, d):
+    rng = np.random.default_rng(41)
+    w = small(dtype, hkv * 4, hkv, d, [300, 17, 40], seed=41, num_blocks=200)
+    dw = DeviceWorkload(w)
+    nb = w.num_blocks
+    perm = rng.permutation(nb)
+    src = perm[:60].astype(np.int32)
+    dst = perm[60:120].astype(np.int32)   # no block is both a source and a destination
+    src[5], dst[7], src[9] = nb + 3, -2, -1  # skipped pairs
+    pkv.paged_kv_copy_blocks(to_dev(src, dtype), to_dev(dst, dtype), dw.k_cache, dw.v_cache)
+    torch().cuda.synchronize()
+    rk, rv = oracle.copy_blocks(w.k_cache, w.v_cache, src, dst)
+    assert bits(dw.k_cache).tobytes() == rk.tobytes()
+    assert bits(dw.v_cache).tobytes() == rv.tobytes()
+
+
+def test_copy_on_write_fork_then_append():
+    """Two sequences share a partially filled last block; the second forks it
+    (copy to a fresh block, table updated) and appends its new token there: the
+    first sequence's block is untouched and both decode to the oracle."""
+    rng = np.random.Generator(np.random.PCG64(42))
+    seqs = [SeqSpec(40, n_new=0, shared_prefix=True), SeqSpec(40, n_new=0, shared_prefix=True)]
+    w = build("cow", 42, "bf16", 32, 8, 128, seqs, shared_prefix_blocks=2, num_blocks=16, rng=rng)
+    tables = w.block_tables.copy()
+    shared_last = int(tables[0, 2])
+    tables[1, 2] = shared_last          # both sequences hold the partial block
+    used = set(tables.ravel().tolist())
+    fresh = next(b for b in range(w.num_blocks) if b not in used)
+    tables[1, 2] = fresh                # the fork: sequence 1 gets its own copy
+    say("copy-on-write fork", shared_last, "->", fresh)
+    dw = DeviceWorkload(w)
+    pkv.paged_kv_copy_blocks(to_dev(np.array([shared_last], np.int32), "bf16"),
+                             to_dev(np.array([fresh], np.int32), "bf16"), dw.k_cache, dw.v_cache)
+    # sequence 1 appends its token 40 at offset 8 of its own copy
+    new = np.random.default_rng(5).standard_normal((1, 8, 128)).astype(np.float32)
+    nk = workloads.f32_to_bf16_bits(new)
+    nv = workloads.f32_to_bf16_bits(new * 0.5)
+    slot = np.array([fresh * 16 + 8], np.int32)
+    pkv.paged_kv_write(to_dev(nk, "bf16"), to_dev(nv, "bf16"), to_dev(slot, "bf16"), dw.k_cache, dw.v_cache)
+    lens = np.array([40, 41], np.int32)
+    out = empty_like_q(w.q.shape, w.dtype)
+    pkv.paged_attn_decode(dw.q, dw.k_cache, dw.v_cache, to_dev(tables, "bf16"), to_dev(lens, "bf16"),
+                          float(w.scale), out)
+    torch().cuda.synchronize()
+    rk, rv = oracle.copy_blocks(w.k_cache, w.v_cache, [shared_last], [fresh])
+    rk, rv = oracle.kv_write(rk, rv, nk, nv, slot)
+    assert bits(dw.k_cache)[shared_last].tobytes() == w.k_cache[shared_last].tobytes()  # the sharer is untouched
+    assert bits(dw.k_cache).tobytes() == rk.tobytes() and bits(dw.v_cache).tobytes() == rv.tobytes()
+    check_attn(values(out), oracle.decode(w.q, rk, rv, tables, lens, w.scale, w.dtype), "bf16", "after fork")
+
+
+def test_block_pool_serving_run_on_device():
+    """Parallel sampling on the device: sequences fork (shared blocks), every step
+    each live sequence appends one token (block copies first, then one batched
+    write) and the batch decodes; the cache and the outputs match the oracle
+    applying the same copies and writes."""
+    rng = np.random.default_rng(77)
+    hq, hkv, d, nblocks, max_blocks = 32, 8, 128, 96, 16
+    pool = pkv.BlockPool(nblocks)
+    kc_h = np.zeros((nblocks, hkv, 16, d), np.uint16)
+    vc_h = np.zeros_like(kc_h)
+    kc, vc = to_dev(kc_h, "bf16"), to_dev(vc_h, "bf16")
+    tables, lens = {}, {}
+    for sid in range(3):  # three prompts of 37, 16 and 50 tokens
+        tables[sid], lens[sid] = np.full(max_blocks, -1, np.int32), 0
+    prompt = {0: 37, 1: 16, 2: 50}
+    scale = 1.0 / np.sqrt(d)
+    n_copies = 0
+    for step in range(40):
+        if step in (1, 9, 20):  # parallel samples: fork children from live parents
+            for parent in list(tables)[:3]:
+                sid = max(tables) + 1
+                tables[sid] = np.full(max_blocks, -1, np.int32)
+                pool.fork(tables[parent], -(-lens[parent] // 16), tables[sid])
+                lens[sid] = lens[parent]
+        src, dst, slots = [], [], []
+        for sid in sorted(tables):
+            n_new = prompt.get(sid, 0) if step == 0 else 1
+            for _ in range(n_new):
+                slot, cp = pool.append_slot(tables[sid], lens[sid])
+                if cp is not None:
+                    src.append(cp[0]); dst.append(cp[1])
+                slots.append(slot)
+                lens[sid] += 1
+        n_copies += len(src)
+        new = workloads.f32_to_bf16_bits(rng.standard_normal((2, len(slots), hkv, d)).astype(np.float32))
+        sl = np.array(slots, np.int32)
+        if src:
+            pkv.paged_kv_copy_blocks(to_dev(np.array(src, np.int32), "bf16"), to_dev(np.array(dst, np.int32), "bf16"),
+                                     kc, vc)
+            kc_h, vc_h = oracle.copy_blocks(kc_h, vc_h, src, dst)
+        pkv.paged_kv_write(to_dev(new[0], "bf16"), to_dev(new[1], "bf16"), to_dev(sl, "bf16"), kc, vc)
+        kc_h, vc_h = oracle.kv_write(kc_h, vc_h, new[0], new[1], sl)
+        ids = sorted(tables)
+        tab = np.stack([tables[s] for s in ids]).astype(np.int32)
+        tab[tab < 0] = 0
+        ln = np.array([lens[s] for s in ids], np.int32)
+        q = workloads.f32_to_bf16_bits(rng.standard_normal((len(ids), hq, d)).astype(np.float32))
+        out = empty_like_q(q.shape, "bf16")
+        pkv.paged_attn_decode(to_dev(q, "bf16"), kc, vc, to_dev(tab, "bf16"), to_dev(ln, "bf16"), float(scale), out)
+        torch().cuda.synchronize()
+        if step % 8 == 7 or step == 39:
+            say("block pool step", step, "live", len(ids), "copies so far", n_copies)
+            assert bits(kc).tobytes() == kc_h.tobytes() and bits(vc).tobytes() == vc_h.tobytes()
+            check_attn(values(out), oracle.decode(q, kc_h, vc_h, tab, ln, scale, "bf16"), "bf16", f"step {step}")
+    assert n_copies >= 4

@@ -350,3 +350,31 @@ def test_shared_prefix_decode_brute_force():
             vals = [list(map(float, full_v[s][t, g])) for t in range(pre + suffix[s])]
             ref = bruteforce.attend_one(list(map(float, q[s, h])), keys, vals, oracle.exact_scale(0.35))
             np.testing.assert_allclose(got[s, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_copy_blocks_element_loop_and_invariance():
+    """Block copy against an element-by-element loop; decode through copied blocks
+    equals decode through the originals; invalid pairs are skipped; NaN payloads survive."""
+    rng = np.random.default_rng(23)
+    nb, hkv, d = 12, 2, 4
+    kc = rng.standard_normal((nb, hkv, 16, d)).astype(np.float32)
+    vc = rng.standard_normal((nb, hkv, 16, d)).astype(np.float32)
+    kc[3, 1, 5, 2] = np.float32(np.nan)
+    src = np.array([3, 0, 7, 99, 4], dtype=np.int32)
+    dst = np.array([9, 10, 11, 2, -1], dtype=np.int32)
+    k2, v2 = oracle.copy_blocks(kc, vc, src, dst)
+    ek, ev = kc.copy(), vc.copy()
+    for s, t in zip(src, dst):
+        if 0 <= s < nb and 0 <= t < nb:
+            for h in range(hkv):
+                for o in range(16):
+                    for e in range(d):
+                        ek[t, h, o, e] = kc[s, h, o, e]
+                        ev[t, h, o, e] = vc[s, h, o, e]
+    assert k2.view(np.uint32).tobytes() == ek.view(np.uint32).tobytes()
+    assert v2.view(np.uint32).tobytes() == ev.view(np.uint32).tobytes()
+    assert np.isnan(k2[9, 1, 5, 2])
+    q = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    a = oracle.decode(q, k2, v2, np.array([[0, 7]], dtype=np.int32), np.array([30]), 0.5, "f32")
+    b = oracle.decode(q, k2, v2, np.array([[10, 11]], dtype=np.int32), np.array([30]), 0.5, "f32")
+    assert np.array_equal(a, b)

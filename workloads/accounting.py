@@ -56,6 +56,12 @@ def write_bytes(num_tokens: int, num_kv_heads: int, head_dim: int, elem_bytes: i
     return 2 * rows + 4 * num_tokens
 
 
+def copy_bytes(num_pairs: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """Algorithmic bytes of a block copy: each pair's K and V block read and written, the two ids read."""
+    block = num_kv_heads * BLOCK_SIZE * head_dim * elem_bytes
+    return num_pairs * (2 * 2 * block + 8)
+
+
 def prefill_flops(chunk_start, context_lens, num_q_heads: int, head_dim: int) -> int:
     """FLOPs of the causal (query, key) pairs of a set of prefill chunks (QK^T and PV, 2 each)."""
     pairs = 0

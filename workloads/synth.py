@@ -345,6 +345,22 @@ def long_context(seed: Optional[int] = None, batch: int = 8, lo: int = 32768, hi
                  description=f"{batch} seqs, L~U{{{lo}..{hi}}}, 64q/8kv x 128, bf16, 90% pool fill")
 
 
+def spec_verify(seed: Optional[int] = None, batch: int = 64, k: int = 4, lo: int = 128,
+                hi: int = 4096) -> Workload:
+    """Speculative-decoding verify step: 64 seqs with accepted contexts L ~ U{128..4096}
+    (the last accepted token included) and k = 4 draft tokens each, so k + 1 = 5 new
+    causal rows per sequence; 32 q / 8 kv heads x 128, bf16.  Not one of the five
+    serving mixes: the verify pass is the prefill-chunk call with 5-row chunks."""
+    seed = SEED_BASE + 6 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(lo, hi + 1, size=batch)
+    seqs = [SeqSpec(int(L) + k, n_new=k + 1, kind="chunk") for L in lens]
+    return build(f"spec-verify-k{k}-bf16", seed, "bf16", 32, 8, 128, seqs, max_blocks_chunk=-(-(hi + k) // BLOCK_SIZE),
+                 chunk_len_max=k + 1, rng=rng,
+                 description=f"{batch} seqs, accepted L~U{{{lo}..{hi}}} + {k} drafts ({k + 1} causal rows each), "
+                             "32q/8kv x 128, bf16")
+
+
 CONFIGS = {
     1: tiny_f32,
     2: llama8b_decode,
@@ -354,5 +370,14 @@ CONFIGS = {
 }
 
 
-def make(cfg_id: int, **kw) -> Workload:
+# Supplementary workloads for the rows beyond the five mixes, by name.
+SUPPLEMENTARY = {
+    "spec-verify": spec_verify,
+}
+
+
+def make(cfg_id, **kw) -> Workload:
+    """A serving mix by number (1..5) or a supplementary workload by name."""
+    if isinstance(cfg_id, str):
+        return SUPPLEMENTARY[cfg_id](**kw)
     return CONFIGS[cfg_id](**kw)
