@@ -4,3 +4,4 @@ from .paged_attention import (  # noqa: F401
     kv_head_of, kv_write, lse_merge, max_abs_err, max_rownorm_rel_err, partition_partials,
     prefill_chunk, slot_location, to_f64, token_location,
 )
+from . import fp8_cache  # noqa: F401,E402
