@@ -77,6 +77,8 @@ def parse():
     p.add_argument("--cold", action="store_true", help="overwrite 512 MB before every step (LLC-cold timing)")
     p.add_argument("--no-cascade", action="store_true",
                    help="shared-prefix workload: plain decode over the full tables instead of the shared-prefix call")
+    p.add_argument("--kv-dtype", choices=["model", "fp8"], default="model",
+                   help="fp8: the cache held as E4M3 codes with per-(slot, kv head) scales (decode workloads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     p.add_argument("--copy-pairs", type=int, default=512,
@@ -113,7 +115,15 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    kc, vc = to_dev(w.k_cache), to_dev(w.v_cache)
+    fp8 = args.kv_dtype == "fp8"
+    if fp8:
+        if w.dtype != "bf16" or w.num_chunks or w.shared_blocks is not None:
+            raise SystemExit("--kv-dtype fp8 takes the bf16 decode workloads without chunks or a shared prefix")
+        pool = workloads.fp8_pool(w)
+        kc, vc = (torch.from_numpy(pool["k_cache"]).to(dev), torch.from_numpy(pool["v_cache"]).to(dev))
+        ksc, vsc = (torch.from_numpy(pool["k_scale"]).to(dev), torch.from_numpy(pool["v_scale"]).to(dev))
+    else:
+        kc, vc = to_dev(w.k_cache), to_dev(w.v_cache)
     nk, nv, slots = to_dev(w.new_k), to_dev(w.new_v), to_dev(w.slot_mapping)
     q, tables, lens = to_dev(w.q), to_dev(w.block_tables), to_dev(w.context_lens)
     out = torch.empty_like(q)
@@ -140,10 +150,16 @@ def main():
     scale = float(w.scale)
 
     def write():
-        pkv.paged_kv_write(nk, nv, slots, kc, vc)
+        if fp8:
+            pkv.paged_kv_write_fp8(nk, nv, slots, kc, vc, ksc, vsc)
+        else:
+            pkv.paged_kv_write(nk, nv, slots, kc, vc)
 
     def decode():
-        if cascade:
+        if fp8:
+            pkv.paged_attn_decode_fp8(q, kc, vc, ksc, vsc, tables, lens, scale, out, max_context_len=w.max_context_len,
+                                      partition_tokens=part, workspace=ws)
+        elif cascade:
             pkv.paged_attn_decode_shared_prefix(q, kc, vc, prefix, own_tables, own_lens, scale, out, workspace=ws)
         else:
             pkv.paged_attn_decode(q, kc, vc, tables, lens, scale, out, max_context_len=w.max_context_len,
@@ -209,8 +225,9 @@ def main():
         dec = {"kv": kv_bytes, "total": pb}
         n_seq, launch_ms = w.num_chunks, pre_ms
     else:
-        dec = accounting.decode_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
-                                      block_tables=w.block_tables, dedupe_shared=(cfg == 4))
+        dec = accounting.decode_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, 1 if fp8 else eb,
+                                      block_tables=w.block_tables, dedupe_shared=(cfg == 4), q_bytes=eb,
+                                      scale_bytes=4 if fp8 else 0)
         kv_bytes = dec["kv"]
         n_seq, launch_ms = w.num_seqs, dec_ms
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -218,14 +235,16 @@ def main():
     achieved = dec["total"] / (launch_ms * 1e-3) / 1e9 if launch_ms > 0 else 0.0
     tr = TRAFFIC.get(w.name)
     traffic = None
-    if tr is not None and tr["sources_sha256"] == sources_sha256() and part == 0 and not args.cold:
+    if tr is not None and tr["sources_sha256"] == sources_sha256() and part == 0 and not args.cold and not fp8:
         traffic = tr["read_bytes"] + tr["write_bytes"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "paged_attn_prefill_chunk: prefill_mfma_kernel" if verify else
                           ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
                            "decode_balanced_kernel + decode_balanced_merge_kernel") if cascade else
-                          ("paged_attn_decode: decode_balanced_kernel + decode_balanced_merge_kernel"
+                          ("paged_attn_decode_fp8: decode_balanced_kernel<fp8> + decode_balanced_merge_kernel"
+                           if fp8 and part == 0 else
+                           "paged_attn_decode: decode_balanced_kernel + decode_balanced_merge_kernel"
                            if part == 0 else "paged_attn_decode: decode_partition_kernel + decode_merge_kernel"),
                 "algorithmic_bytes_per_launch": dec["total"], "launch_ms_mean": round(launch_ms, 5),
                 "traffic_read_write_bytes": [tr["read_bytes"], tr["write_bytes"]] if traffic else None}
@@ -233,7 +252,8 @@ def main():
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 kv, bf16 q/out" if fp8 else w.dtype,
+        "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "seed": w.seed, "num_seqs": n_seq,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": 16, "num_blocks": w.num_blocks,
@@ -245,6 +265,7 @@ def main():
                              else "") +
                             f"balanced over {pkv.decode_split_waves(w.num_q_heads, w.num_kv_heads)} wavefronts",
                    "kv_bytes_per_step": kv_bytes, "llc": "cold (512 MB overwrite per step)" if args.cold else "warm",
+                   "kv_cache": "E4M3 codes + float32 scale per (slot, kv head)" if fp8 else w.dtype,
                    "layers_per_step": 1},
         "seq_tokens_per_s": round(seq_tok_s, 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -259,7 +280,7 @@ def main():
                           "tflops": round(flops / (pm * 1e-3) / 1e12, 2),
                           "mfma_frac_of_bf16_peak": round(flops / (pm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
-    if args.copy_pairs and not verify:
+    if args.copy_pairs and not verify and not fp8:
         # supplementary: copy-on-write block copies, cached blocks into blocks no table holds
         held = set(np.asarray(w.block_tables).ravel().tolist()) | set(np.asarray(w.chunk_tables).ravel().tolist())
         free = np.array([b for b in range(w.num_blocks) if b not in held], dtype=np.int32)
@@ -280,7 +301,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, cfg)
     print(json.dumps(res), flush=True)
 

@@ -63,6 +63,7 @@ extern "C" {
 
 #define PKV_DTYPE_F32 0
 #define PKV_DTYPE_BF16 1
+#define PKV_DTYPE_FP8_E4M3 2 /* quantised cache: the *_fp8 entry points only */
 #define PKV_BLOCK_SIZE 16
 
 /* Description of one layer's paged cache (both K and V use it). */
@@ -71,7 +72,7 @@ typedef struct pkv_cache_desc {
   int32_t block_size;   /* tokens per block; must be 16 */
   int32_t num_kv_heads; /* >= 1 */
   int32_t head_dim;     /* 64 or 128 */
-  int32_t dtype;        /* PKV_DTYPE_F32 or PKV_DTYPE_BF16 */
+  int32_t dtype;        /* PKV_DTYPE_F32, PKV_DTYPE_BF16, or PKV_DTYPE_FP8_E4M3 (*_fp8 calls) */
 } pkv_cache_desc;
 
 /*
@@ -109,6 +110,50 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
  */
 int paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* cache, const int32_t* src_blocks,
                          const int32_t* dst_blocks, int64_t num_pairs, void* hip_stream);
+
+/*
+ * fp8 KV cache.  ("Part 47 | Inference basics", chengxuchu.com, section 2.4:
+ * a server short of memory may keep the cache quantised.  The page names no
+ * format; this library's is the following.)  Cache elements are OCP E4M3
+ * bytes -- sign, 4 exponent bits with bias 7, 3 mantissa bits, largest finite
+ * 448, no infinities -- in the same [num_blocks][num_kv_heads][16][head_dim]
+ * layout, with one float32 scale per (slot, kv head):
+ *
+ *   k_scale, v_scale   float32 [num_blocks][num_kv_heads][16] (device)
+ *   value of element d of a slot's row = e4m3(code_d) * scale
+ *
+ * The descriptor's dtype is PKV_DTYPE_FP8_E4M3; queries and outputs are
+ * bfloat16.  Quantisation (paged_kv_write_fp8), per new row of one kv head,
+ * in float32:  amax = max |x|,  scale = amax / 448,  inv = 448 / amax (0 when
+ * amax is 0),  code = the E4M3 value nearest to clamp(x * inv, -448, 448),
+ * ties to the even code.  The codes and scales are reproducible bit for bit;
+ * each write touches only its own slots.
+ *
+ * paged_kv_write_fp8: as paged_kv_write, from k, v [num_tokens][num_kv_heads]
+ *   [head_dim] of in_dtype (PKV_DTYPE_BF16 or PKV_DTYPE_F32), storing codes
+ *   and scales.  Rows must be finite.
+ * paged_attn_decode_fp8: as paged_attn_decode over the dequantised cache
+ *   (workspace sizes from paged_attn_decode_workspace_bytes).  Each token's K
+ *   scale multiplies its scores and its V scale its weights, so the codes are
+ *   widened exactly and never rescaled element by element.
+ * paged_kv_copy_blocks_fp8: as paged_kv_copy_blocks, copying the blocks'
+ *   codes and their scales.
+ *
+ * The prefill-chunk and shared-prefix calls take float32 / bfloat16 caches
+ * only.  Errors as for the unquantised calls; PKV_ERR_DTYPE for a descriptor
+ * that is not PKV_DTYPE_FP8_E4M3 or an in_dtype other than bf16 / f32.
+ */
+int paged_kv_write_fp8(const void* k, const void* v, int32_t in_dtype, const int32_t* slot_mapping,
+                       int64_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                       const pkv_cache_desc* cache, void* hip_stream);
+int paged_attn_decode_fp8(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                          const void* v_cache, const float* k_scale, const float* v_scale,
+                          const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                          int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream);
+int paged_kv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                             const pkv_cache_desc* cache, const int32_t* src_blocks, const int32_t* dst_blocks,
+                             int64_t num_pairs, void* hip_stream);
 
 /*
  * Host-side block bookkeeping for copy-on-write sharing (same "PagedAttention"
@@ -272,7 +317,7 @@ const char* pkv_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION ((1 << 16) | 2)
+#define PKV_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

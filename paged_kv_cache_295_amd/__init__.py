@@ -17,6 +17,7 @@ __all__ = [
     "PagedKVError", "load_library", "paged_kv_write", "paged_attn_decode", "paged_attn_prefill_chunk",
     "decode_workspace_bytes", "decode_split_waves", "library_path", "BLOCK_SIZE",
     "paged_attn_decode_shared_prefix", "shared_prefix_workspace_bytes", "paged_kv_copy_blocks", "BlockPool",
+    "paged_kv_write_fp8", "paged_attn_decode_fp8", "paged_kv_copy_blocks_fp8",
 ]
 
 BLOCK_SIZE = 16
@@ -26,6 +27,7 @@ _lib = None
 
 PKV_DTYPE_F32 = 0
 PKV_DTYPE_BF16 = 1
+PKV_DTYPE_FP8_E4M3 = 2
 
 
 class PagedKVError(RuntimeError):
@@ -70,6 +72,14 @@ def load_library():
     lib.paged_attn_decode_shared_prefix.argtypes = [vp, i32, i32, vp, vp, cdp, vp, i32, vp, i32, vp, f32, vp, vp, sz,
                                                     vp]
     lib.paged_attn_decode_shared_prefix.restype = ctypes.c_int
+    fp = ctypes.c_void_p
+    lib.paged_kv_write_fp8.argtypes = [vp, vp, i32, vp, i64, vp, vp, fp, fp, cdp, vp]
+    lib.paged_kv_write_fp8.restype = ctypes.c_int
+    lib.paged_attn_decode_fp8.argtypes = [vp, i32, i32, vp, vp, fp, fp, cdp, vp, i32, vp, i32, f32, vp, i32, vp, sz,
+                                          vp]
+    lib.paged_attn_decode_fp8.restype = ctypes.c_int
+    lib.paged_kv_copy_blocks_fp8.argtypes = [vp, vp, fp, fp, cdp, vp, vp, i64, vp]
+    lib.paged_kv_copy_blocks_fp8.restype = ctypes.c_int
     lib.paged_attn_prefill_chunk.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp]
     lib.paged_attn_prefill_chunk.restype = ctypes.c_int
     ip = ctypes.POINTER(i32)
@@ -134,6 +144,21 @@ def _cache_desc(k_cache) -> CacheDesc:
     return CacheDesc(nb, BLOCK_SIZE, hkv, d, _dtype_code(k_cache))
 
 
+def _fp8_desc(k_cache, v_cache, k_scale, v_scale) -> CacheDesc:
+    """Descriptor of an E4M3 cache (uint8 or float8_e4m3fn tensors) with float32 scales [NB, Hkv, 16]."""
+    torch = _torch()
+    fp8_types = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    if k_cache.dtype not in fp8_types or v_cache.dtype != k_cache.dtype:
+        raise TypeError("fp8 caches must be uint8 (E4M3 codes) or float8_e4m3fn")
+    if k_cache.dim() != 4 or k_cache.shape[2] != BLOCK_SIZE or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32 or \
+            k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_cache.shape[:3]:
+        raise ValueError("scales must be float32 [num_blocks, num_kv_heads, 16]")
+    nb, hkv, _, d = k_cache.shape
+    return CacheDesc(nb, BLOCK_SIZE, hkv, d, PKV_DTYPE_FP8_E4M3)
+
+
 def _check(status: int, what: str):
     if status != 0:
         raise PagedKVError(status, what)
@@ -165,6 +190,34 @@ def paged_kv_copy_blocks(src_blocks, dst_blocks, k_cache, v_cache, stream=None):
     st = lib.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _i32(src_blocks, "src_blocks"),
                                   _i32(dst_blocks, "dst_blocks"), src_blocks.shape[0], _stream(stream))
     _check(st, "paged_kv_copy_blocks")
+
+
+def paged_kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream=None):
+    """Quantise row i of k/v ([T, Hkv, D], bf16 or f32) into E4M3 codes + scales at slot slot_mapping[i]."""
+    lib = load_library()
+    desc = _fp8_desc(k_cache, v_cache, k_scale, v_scale)
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    if k.shape[1:] != (desc.num_kv_heads, desc.head_dim) or v.shape != k.shape:
+        raise ValueError("k, v must be [T, num_kv_heads, head_dim] matching the caches")
+    if slot_mapping.shape != (k.shape[0],):
+        raise ValueError("slot_mapping must be [T]")
+    st = lib.paged_kv_write_fp8(_ptr(k), _ptr(v), _dtype_code(k), _i32(slot_mapping, "slot_mapping"), k.shape[0],
+                                _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), ctypes.byref(desc),
+                                _stream(stream))
+    _check(st, "paged_kv_write_fp8")
+
+
+def paged_kv_copy_blocks_fp8(src_blocks, dst_blocks, k_cache, v_cache, k_scale, v_scale, stream=None):
+    """Copy block src_blocks[i] to dst_blocks[i]: codes of both caches and their scales."""
+    lib = load_library()
+    desc = _fp8_desc(k_cache, v_cache, k_scale, v_scale)
+    if src_blocks.dim() != 1 or dst_blocks.shape != src_blocks.shape:
+        raise ValueError("src_blocks and dst_blocks must be [N]")
+    st = lib.paged_kv_copy_blocks_fp8(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                      ctypes.byref(desc), _i32(src_blocks, "src_blocks"),
+                                      _i32(dst_blocks, "dst_blocks"), src_blocks.shape[0], _stream(stream))
+    _check(st, "paged_kv_copy_blocks_fp8")
 
 
 def decode_split_waves(num_q_heads: int, num_kv_heads: int) -> int:
@@ -208,6 +261,35 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
                                int(max_context_len), float(scale), _ptr(out), int(partition_tokens), ws_ptr,
                                ws_bytes, _stream(stream))
     _check(st, "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, out,
+                          max_context_len=None, partition_tokens=0, workspace=None, stream=None):
+    """paged_attn_decode over an E4M3 cache with per-(slot, kv head) scales; q and out bfloat16."""
+    lib = load_library()
+    torch = _torch()
+    desc = _fp8_desc(k_cache, v_cache, k_scale, v_scale)
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("q and out must be bfloat16")
+    B, hq, d = q.shape
+    if out.shape != q.shape or d != desc.head_dim:
+        raise ValueError("q/out must be [B, Hq, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables [B, max_blocks], context_lens [B]")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * BLOCK_SIZE
+    need = decode_workspace_bytes(B, hq, desc.num_kv_heads, d, max_context_len, partition_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.paged_attn_decode_fp8(_ptr(q), B, hq, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                   ctypes.byref(desc), _i32(block_tables, "block_tables"), max_blocks,
+                                   _i32(context_lens, "context_lens"), int(max_context_len), float(scale), _ptr(out),
+                                   int(partition_tokens), ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "paged_attn_decode_fp8")
     return out
 
 

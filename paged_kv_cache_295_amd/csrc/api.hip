@@ -10,9 +10,12 @@ using namespace pkv;
 
 namespace {
 
-int check_cache(const pkv_cache_desc* c) {
+// fp8: the entry points that take scale arrays want an E4M3 cache, the others
+// a float32 or bfloat16 one.
+int check_cache(const pkv_cache_desc* c, bool fp8 = false) {
   if (c == nullptr) return PKV_ERR_NULL;
-  if (c->dtype != PKV_DTYPE_F32 && c->dtype != PKV_DTYPE_BF16) return PKV_ERR_DTYPE;
+  if (fp8 ? c->dtype != PKV_DTYPE_FP8_E4M3 : (c->dtype != PKV_DTYPE_F32 && c->dtype != PKV_DTYPE_BF16))
+    return PKV_ERR_DTYPE;
   if (c->block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PKV_ERR_SHAPE;
@@ -127,15 +130,22 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
   return partition_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens);
 }
 
-int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache, const void* v_cache,
-                      const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                      const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
-                      int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream) {
-  int st = check_cache(cache);
+}  // extern "C"
+
+namespace {
+
+int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                  const float* k_scale, const float* v_scale, const pkv_cache_desc* cache,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                  int32_t max_context_len, float scale, void* out, int32_t partition_tokens, void* workspace,
+                  size_t workspace_bytes, void* hip_stream) {
+  const bool fp8 = k_scale != nullptr || v_scale != nullptr;
+  int st = check_cache(cache, fp8);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (fp8 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
   if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (max_blocks_per_seq <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
@@ -172,7 +182,65 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
   a.max_parts = (int32_t)max_parts64;
   a.scale_log2 = scale * kLog2eHost;
   a.balanced_waves = balanced ? balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads)) : 0;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   return from_hip(launch_decode(a, as_stream(hip_stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                      const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                      int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return decode_common(q, num_seqs, num_q_heads, k_cache, v_cache, nullptr, nullptr, cache, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, scale, out, partition_tokens, workspace,
+                       workspace_bytes, hip_stream);
+}
+
+int paged_attn_decode_fp8(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                          const void* v_cache, const float* k_scale, const float* v_scale,
+                          const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                          int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!k_scale || !v_scale) return PKV_ERR_NULL;
+  return decode_common(q, num_seqs, num_q_heads, k_cache, v_cache, k_scale, v_scale, cache, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, scale, out, partition_tokens, workspace,
+                       workspace_bytes, hip_stream);
+}
+
+int paged_kv_write_fp8(const void* k, const void* v, int32_t in_dtype, const int32_t* slot_mapping,
+                       int64_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                       const pkv_cache_desc* cache, void* hip_stream) {
+  int st = check_cache(cache, true);
+  if (st != PKV_OK) return st;
+  if (in_dtype != PKV_DTYPE_F32 && in_dtype != PKV_DTYPE_BF16) return PKV_ERR_DTYPE;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale) return PKV_ERR_NULL;
+  WriteArgs a{k, v, slot_mapping, num_tokens, k_cache, v_cache, cache->num_blocks, cache->num_kv_heads,
+              cache->head_dim, cache->dtype};
+  return from_hip(launch_kv_write_fp8(a, in_dtype, k_scale, v_scale, as_stream(hip_stream)));
+}
+
+int paged_kv_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                             const pkv_cache_desc* cache, const int32_t* src_blocks, const int32_t* dst_blocks,
+                             int64_t num_pairs, void* hip_stream) {
+  int st = check_cache(cache, true);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !src_blocks || !dst_blocks) return PKV_ERR_NULL;
+  const int64_t code_bytes = (int64_t)cache->num_kv_heads * PKV_BLOCK_SIZE * cache->head_dim;
+  const int64_t scale_bytes = (int64_t)cache->num_kv_heads * PKV_BLOCK_SIZE * (int64_t)sizeof(float);
+  hipStream_t s = as_stream(hip_stream);
+  hipError_t e = launch_kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, num_pairs, cache->num_blocks,
+                                       code_bytes, s);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  return from_hip(launch_kv_copy_blocks(k_scale, v_scale, src_blocks, dst_blocks, num_pairs, cache->num_blocks,
+                                        scale_bytes, s));
 }
 
 size_t paged_attn_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -67,14 +67,18 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int64_t row) {
   return r;
 }
 
-template <typename T, int D, int GB, int LPT>
+template <typename KV, int D, int GB, int LPT>
 struct DecodeShape {
-  using E = Elem<T>;
-  static constexpr int kEPC = E::kPerChunk;       // elements per 16-byte chunk
-  static constexpr int kRowChunks = D / kEPC;     // chunks per token row of one kv head
-  static constexpr int kCPL = kRowChunks / LPT;   // chunks per lane per token
-  static constexpr int kTPP = kWave / LPT;        // tokens covered by one load pass
-  static constexpr int kNPass = kBlock / kTPP;    // tokens per lane per block
+  using E = Elem<KV>;
+  using Q = typename KvTraits<KV>::Q;                   // query / output element
+  static constexpr int kElemBytes = KvTraits<KV>::kElemBytes;
+  static constexpr int kRowBytes = D * kElemBytes;      // one token row of one kv head
+  static constexpr int kEPC = E::kPerChunk;             // cache elements per 16-byte chunk
+  static constexpr int kQPC = kEPC * (int)sizeof(Q) / 16;  // query chunks holding the same dims
+  static constexpr int kRowChunks = D / kEPC;           // chunks per token row of one kv head
+  static constexpr int kCPL = kRowChunks / LPT;         // chunks per lane per token
+  static constexpr int kTPP = kWave / LPT;              // tokens covered by one load pass
+  static constexpr int kNPass = kBlock / kTPP;          // tokens per lane per block
   static_assert(kRowChunks % LPT == 0 && kCPL >= 1, "LPT must divide the chunks of a row");
   static_assert(kBlock % kTPP == 0, "a block must be a whole number of passes");
 };
@@ -89,8 +93,9 @@ constexpr bool kStreamKV = PKV_DECODE_STREAM_KV != 0;
 // acc[h][c][e] += sum_p prob[p][h] * V[p][c][e].  float32 uses plain FMAs; bf16
 // rounds the probabilities to bf16 and pairs two tokens per v_dot2_f32_bf16
 // (the matrix-core prefill rounds P the same way), which halves the ALU work
-// of the PV product.
-template <typename T, int NP, int CPL, int GB>
+// of the PV product.  E4M3 codes are widened exactly to bf16 pairs first, and
+// prob already carries each token's V scale.
+template <typename KV, int NP, int CPL, int GB>
 struct PV;
 
 template <int NP, int CPL, int GB>
@@ -136,6 +141,56 @@ struct PV<__bf16, NP, CPL, GB> {
   }
 };
 
+template <int NP, int CPL, int GB>
+struct PV<Fp8E4M3, NP, CPL, GB> {
+  __device__ __forceinline__ static void apply(const float (&prob)[NP][GB], const Chunk (&vv)[NP][CPL],
+                                               float (&acc)[GB][CPL][16]) {
+    if constexpr (NP % 2 == 0) {
+#pragma unroll
+      for (int p = 0; p < NP; p += 2) {
+        bf16x2_t pp[GB];
+#pragma unroll
+        for (int h = 0; h < GB; ++h) pp[h] = __builtin_bit_cast(bf16x2_t, pack_bf16x2(prob[p][h], prob[p + 1][h]));
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {  // dims 4w + 2hi, 4w + 2hi + 1
+              const uint32_t a0 = hi ? fp8x2_to_bf16x2<true>(vv[p][c].w[w]) : fp8x2_to_bf16x2<false>(vv[p][c].w[w]);
+              const uint32_t a1 =
+                  hi ? fp8x2_to_bf16x2<true>(vv[p + 1][c].w[w]) : fp8x2_to_bf16x2<false>(vv[p + 1][c].w[w]);
+              const bf16x2_t ev = __builtin_bit_cast(bf16x2_t, (a0 & 0xffffu) | (a1 << 16));
+              const bf16x2_t od = __builtin_bit_cast(bf16x2_t, (a0 >> 16) | (a1 & 0xffff0000u));
+              const int e = 4 * w + 2 * hi;
+#pragma unroll
+              for (int h = 0; h < GB; ++h) {
+                acc[h][c][e] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], ev, acc[h][c][e], false);
+                acc[h][c][e + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], od, acc[h][c][e + 1], false);
+              }
+            }
+      }
+    } else {  // one token per lane per block: widened values, plain FMAs
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+              const uint32_t b = hi ? fp8x2_to_bf16x2<true>(vv[p][c].w[w]) : fp8x2_to_bf16x2<false>(vv[p][c].w[w]);
+              const int e = 4 * w + 2 * hi;
+#pragma unroll
+              for (int h = 0; h < GB; ++h) {
+                acc[h][c][e] = fmaf(prob[p][h], bf16_lo(b), acc[h][c][e]);
+                acc[h][c][e + 1] = fmaf(prob[p][h], bf16_hi(b), acc[h][c][e + 1]);
+              }
+            }
+    }
+  }
+};
+
 // All-reduce every score over the LPT lanes of its token, one DPP step at a
 // time across all scores so that consecutive DPP reads never depend on the
 // instruction right before them.
@@ -168,39 +223,51 @@ constexpr float kRescaleSlack = 8.0f;
 // One wave's attention state for GB query heads of one kv head over a run of
 // consecutive blocks of one sequence (a "segment"): the query chunks, and per
 // token group the running max m (log2 units), sum l and unnormalised output.
-template <typename T, int D, int GB, int LPT, int NS>
+template <typename KV, int D, int GB, int LPT, int NS>
 struct Segment {
-  using S = DecodeShape<T, D, GB, LPT>;
+  using S = DecodeShape<KV, D, GB, LPT>;
   using E = typename S::E;
-  static constexpr int EPC = S::kEPC, CPL = S::kCPL, TPP = S::kTPP, NP = S::kNPass;
+  using T = typename S::Q;
+  static constexpr int EPC = S::kEPC, CPL = S::kCPL, TPP = S::kTPP, NP = S::kNPass, QPC = S::kQPC;
+  static constexpr int RB = S::kRowBytes;
+  static constexpr bool kScaled = KvTraits<KV>::kScaled;
+  // scales carried per stage (one dummy entry when there are none)
+  static constexpr int NSC = kScaled ? NP : 1;
 
-  Chunk qv[GB][CPL];
+  Chunk qv[GB][CPL][QPC];
   float m[GB], l[GB], acc[GB][CPL][EPC];
   bool bad_block;
   int tg, li;
   int lane_base;  // byte offset of this lane's first chunk inside a tile
   const char* __restrict__ kc;
   const char* __restrict__ vc;
+  const float* __restrict__ ksc;  // per-(slot, kv head) scales of scaled caches
+  const float* __restrict__ vsc;
   float sl2;
 
-  static constexpr int64_t kTileBytes = (int64_t)kBlock * D * sizeof(T);
+  static constexpr int64_t kTileBytes = (int64_t)kBlock * RB;
 
   __device__ __forceinline__ explicit Segment(const DecodeArgs& a) {
     const int lane = __lane_id();
     tg = lane / LPT;
     li = lane % LPT;
-    lane_base = tg * (D * (int)sizeof(T)) + li * 16;
+    lane_base = tg * RB + li * 16;
     kc = reinterpret_cast<const char*>(a.k_cache);
     vc = reinterpret_cast<const char*>(a.v_cache);
+    ksc = a.k_scale;
+    vsc = a.v_scale;
     sl2 = a.scale_log2;
   }
 
   // The chunks of the GB query rows at qrow (head h0 of the row) this lane multiplies.
   __device__ __forceinline__ void load_q(const T* __restrict__ qrow) {
+    constexpr int QE = 16 / (int)sizeof(T);  // query elements per chunk
 #pragma unroll
     for (int h = 0; h < GB; ++h)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) qv[h][c] = load_chunk(qrow + h * D + (c * LPT + li) * EPC);
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int j = 0; j < QPC; ++j) qv[h][c][j] = load_chunk(qrow + h * D + (c * LPT + li) * EPC + j * QE);
   }
 
   __device__ __forceinline__ void reset() {
@@ -220,12 +287,13 @@ struct Segment {
   // the caches.  Every tile is loaded whole (rows past the context in a last
   // block are still inside it): one constant per-lane offset plus immediates,
   // so no address arithmetic sits between the loads of consecutive tiles.
-  __device__ __forceinline__ void load_tile(Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], int64_t off) const {
+  __device__ __forceinline__ void load_tile(Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], float (&sk)[NSC],
+                                            float (&sv)[NSC], int64_t off) const {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const int o = lane_base + p * TPP * (D * (int)sizeof(T)) + c * LPT * 16;
+        const int o = lane_base + p * TPP * RB + c * LPT * 16;
         if constexpr (kStreamKV) {
           kk[p][c] = load_chunk_stream(kc + off + o);
           vv[p][c] = load_chunk_stream(vc + off + o);
@@ -234,11 +302,21 @@ struct Segment {
           vv[p][c] = load_chunk(vc + off + o);
         }
       }
+    if constexpr (kScaled) {
+      // the tile's 16 scales sit at (block * kv heads + kv head) * 16, i.e. off / RB
+      const int64_t so = off / RB + tg;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        sk[p] = __builtin_nontemporal_load(ksc + so + p * TPP);
+        sv[p] = __builtin_nontemporal_load(vsc + so + p * TPP);
+      }
+    }
   }
 
   // Attend the query rows over one tile whose first token (of this lane's
   // pass 0) is tok0; tokens at or past `end` are masked.
-  __device__ __forceinline__ void compute(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL], int tok0, int end) {
+  __device__ __forceinline__ void compute(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
+                                          const float (&sk)[NSC], const float (&sv)[NSC], int tok0, int end) {
     float x[NP * GB];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -252,9 +330,12 @@ struct Segment {
     group_sum_all<LPT>(x);
     float sc[NP][GB];
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int p = 0; p < NP; ++p) {
+      // scaled caches: the token's K scale multiplies its dot products
+      const float f = kScaled ? sk[kScaled ? p : 0] * sl2 : sl2;
 #pragma unroll
-      for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? x[p * GB + h] * sl2 : -__builtin_inff();
+      for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? x[p * GB + h] * f : -__builtin_inff();
+    }
     bool need = false;
     float bm[GB];
 #pragma unroll
@@ -299,8 +380,13 @@ struct Segment {
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int w = 0; w < 4; ++w) vz[p][c].w[w] = ok ? vv[p][c].w[w] : 0u;
+      if constexpr (kScaled) {  // the V scale joins the weights (the sums l keep the plain ones)
+        const float f = ok ? sv[kScaled ? p : 0] : 0.0f;
+#pragma unroll
+        for (int h = 0; h < GB; ++h) sc[p][h] *= f;
+      }
     }
-    PV<T, NP, CPL, GB>::apply(sc, vz, acc);
+    PV<KV, NP, CPL, GB>::apply(sc, vz, acc);
   }
 
   // Start from the attention state of a shared prefix: the a.init_splits
@@ -364,6 +450,7 @@ struct Segment {
     // are masked and add exactly nothing.  Table entries are fetched one pass
     // ahead.
     Chunk kS[NS][NP][CPL], vS[NS][NP][CPL];
+    float skS[NS][NSC], svS[NS][NSC];
     const int last = nblk - 1;
     int64_t offs[NS];
     int first[2 * NS];  // the first 2 NS entries, fetched together
@@ -371,7 +458,7 @@ struct Segment {
     for (int i = 0; i < 2 * NS; ++i) first[i] = table[min(i, last)];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      load_tile(kS[st], vS[st], tile_off(first[st]));
+      load_tile(kS[st], vS[st], skS[st], svS[st], tile_off(first[st]));
       // each stage's loads are issued before the next stage's: waits are in order
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -380,9 +467,9 @@ struct Segment {
     for (int jb = 0;; jb += NS) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        compute(kS[st], vS[st], (blk0 + jb + st) * kBlock + tg, end);
+        compute(kS[st], vS[st], skS[st], svS[st], (blk0 + jb + st) * kBlock + tg, end);
         const int64_t next = block_off(min(jb + 2 * NS + st, last));
-        load_tile(kS[st], vS[st], offs[st]);
+        load_tile(kS[st], vS[st], skS[st], svS[st], offs[st]);
         offs[st] = next;
       }
       if (jb + NS >= nblk) break;
@@ -392,7 +479,7 @@ struct Segment {
   // Combine the 64 / LPT token-group streams (every lane ends with the totals):
   // agree on the largest running max, rescale to it, then add.
   __device__ __forceinline__ void merge_groups() {
-    static_assert(LPT == 8 || LPT == 16, "token groups differ in lane bits 3..5 or 4..5");
+    static_assert(LPT == 4 || LPT == 8 || LPT == 16, "token groups differ in lane bits 2..5, 3..5 or 4..5");
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
       const float M = groups_max<LPT>(m[h]);
@@ -413,13 +500,16 @@ struct Segment {
     for (int h = 0; h < GB; ++h) {
       if (tg != h % TPP) continue;
       const float inv = bad_block ? nan : 1.0f / l[h];
+      constexpr int QE = 16 / (int)sizeof(T);  // output elements per chunk
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        float o[EPC];
+      for (int c = 0; c < CPL; ++c)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) o[e] = acc[h][c][e] * inv;
-        store_chunk(outp + h * D + (c * LPT + li) * EPC, E::narrow(o));
-      }
+        for (int j = 0; j < QPC; ++j) {
+          float o[QE];
+#pragma unroll
+          for (int e = 0; e < QE; ++e) o[e] = acc[h][c][j * QE + e] * inv;
+          store_chunk(outp + h * D + (c * LPT + li) * EPC + j * QE, Elem<T>::narrow(o));
+        }
     }
   }
 
@@ -454,8 +544,9 @@ struct Segment {
 // Fixed partitions: one wave per (query row, kv head, head subgroup,
 // partition of P tokens).  Also serves float32 prefill rows (one partition
 // covering the whole table).
-template <typename T, int D, int GB, int LPT, int NS>
+template <typename KV, int D, int GB, int LPT, int NS>
 __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a, const int32_t* __restrict__ tables) {
+  using T = typename KvTraits<KV>::Q;
   const int lane = __lane_id();
   const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
   int64_t t = blockIdx.x;
@@ -487,7 +578,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
   const int blk0 = start / kBlock;
   const int nblk = (end - start + kBlock - 1) / kBlock;
 
-  Segment<T, D, GB, LPT, NS> seg(a);
+  Segment<KV, D, GB, LPT, NS> seg(a);
   const T* qrow = reinterpret_cast<const T*>(a.q) + (row * a.num_q_heads + h0) * (int64_t)D;
   seg.run(a, qrow, tables + (int64_t)ri.seq * a.max_blocks_per_seq + blk0, g, blk0, nblk, end);
   seg.merge_groups();
@@ -623,9 +714,10 @@ __device__ __forceinline__ int64_t range_begin(int w, int W, int64_t U) { return
 // The wave whose range holds cost unit u.
 __device__ __forceinline__ int wave_of(int64_t u, int W, int64_t U) { return (int)(((u + 1) * W + U - 1) / U) - 1; }
 
-template <typename T, int D, int GB, int LPT, int NS>
+template <typename KV, int D, int GB, int LPT, int NS>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
                                                               const int32_t* __restrict__ lens) {
+  using T = typename KvTraits<KV>::Q;
   const int lane = __lane_id();
   const int W = gridDim.x;
   const int w = blockIdx.x;
@@ -659,7 +751,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
   s = __builtin_amdgcn_readfirstlane(s);
   cum = uniform64(cum);
 
-  Segment<T, D, GB, LPT, NS> seg(a);
+  Segment<KV, D, GB, LPT, NS> seg(a);
   int L = lens[s];
   int nb = seq_blocks(L, cap);
   bool first = true;
@@ -877,27 +969,28 @@ hipError_t launch_prefix_merge(float* part_o, float* part_ml, int64_t rows, int 
 #ifndef PKV_DECODE_STAGES
 #define PKV_DECODE_STAGES 2
 #endif
-template <typename T, int D, int GB>
+template <typename KV, int D, int GB>
 constexpr int lanes_per_token() {
-  constexpr int row_chunks = D * (int)sizeof(T) / 16;
+  constexpr int row_chunks = D * KvTraits<KV>::kElemBytes / 16;
   constexpr int want = GB >= 8 ? 16 : PKV_DECODE_LPT_SMALL_GROUP;
   return row_chunks < want ? row_chunks : want;
 }
 // Register stages of the K/V prefetch pipeline (fixed partitions).
-template <typename T, int D, int GB>
+template <typename KV, int D, int GB>
 constexpr int pipeline_stages() {
   return PKV_DECODE_STAGES;
 }
 
-template <typename T, int D, int GB>
+template <typename KV, int D, int GB>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int LPT = lanes_per_token<T, D, GB>();
-  constexpr int NS = pipeline_stages<T, D, GB>();
+  using T = typename KvTraits<KV>::Q;
+  constexpr int LPT = lanes_per_token<KV, D, GB>();
+  constexpr int NS = pipeline_stages<KV, D, GB>();
   if (a.balanced_waves > 0) {
     const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
     const int64_t merges = (int64_t)a.num_seqs * a.num_kv_heads * hsubs;
     if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_balanced_kernel<T, D, GB, LPT, NS>), dim3(a.balanced_waves), dim3(64), 0, stream, a,
+    hipLaunchKernelGGL((decode_balanced_kernel<KV, D, GB, LPT, NS>), dim3(a.balanced_waves), dim3(64), 0, stream, a,
                        a.block_tables, a.context_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -910,7 +1003,7 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t items = rows * a.num_kv_heads * hsubs * a.max_parts;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, GB, LPT, NS>), dim3((unsigned)items), dim3(64), 0, stream, a,
+  hipLaunchKernelGGL((decode_partition_kernel<KV, D, GB, LPT, NS>), dim3((unsigned)items), dim3(64), 0, stream, a,
                      a.block_tables);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
@@ -920,13 +1013,13 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename KV, int D>
 static hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
   switch (heads_per_wave(a.num_q_heads / a.num_kv_heads)) {
-    case 1: return launch_typed<T, D, 1>(a, stream);
-    case 2: return launch_typed<T, D, 2>(a, stream);
-    case 4: return launch_typed<T, D, 4>(a, stream);
-    case 8: return launch_typed<T, D, 8>(a, stream);
+    case 1: return launch_typed<KV, D, 1>(a, stream);
+    case 2: return launch_typed<KV, D, 2>(a, stream);
+    case 4: return launch_typed<KV, D, 4>(a, stream);
+    case 8: return launch_typed<KV, D, 8>(a, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -938,6 +1031,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   } else if (a.dtype == 1) {
     if (a.head_dim == 64) return launch_gb<__bf16, 64>(a, stream);
     if (a.head_dim == 128) return launch_gb<__bf16, 128>(a, stream);
+  } else if (a.dtype == 2) {
+    if (a.k_scale == nullptr || a.v_scale == nullptr) return hipErrorInvalidValue;
+    if (a.head_dim == 64) return launch_gb<Fp8E4M3, 64>(a, stream);
+    if (a.head_dim == 128) return launch_gb<Fp8E4M3, 128>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -66,6 +66,110 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// fp8 cache write: quantise each new token's K and V row of one kv head to
+// OCP E4M3 codes with one float scale for the row ("Part 47", section 2.4: a
+// server may keep the cache quantised; the format and the per-(slot, kv head)
+// scale are this library's choice).  Every decision is taken in float32 in a
+// fixed order, so the codes are reproducible bit for bit:
+//   amax = max |x|, scale = amax / 448, inv = 448 / amax (0 if amax == 0),
+//   y = clamp(x * inv, -448, 448), code = nearest E4M3 value, ties to even.
+// One wave per (token, kv head); lane i holds dims i * NPL .. i * NPL + NPL - 1.
+
+// E4M3 code of y, |y| <= 448, rounded to nearest with ties to the even code.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a < 0.015625f) {  // below 2^-6: the subnormal codes m * 2^-9, m = 0 .. 8 (8 is 2^-6 itself)
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // a = 2^e * (1 + f)
+  float m = __builtin_rintf(ldexpf(a, 3 - e));               // 8 .. 16: implicit bit + 3 mantissa bits
+  if (m == 16.0f) {
+    ++e;
+    m = 8.0f;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | ((uint32_t)m - 8u);
+}
+
+template <int D, typename In>
+__global__ __launch_bounds__(256) void kv_write_fp8_kernel(const In* __restrict__ k, const In* __restrict__ v,
+                                                           const int32_t* __restrict__ slots, int64_t num_tokens,
+                                                           uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                           float* __restrict__ k_scale, float* __restrict__ v_scale,
+                                                           int32_t num_blocks, int32_t num_kv_heads) {
+  constexpr int NPL = D / kWave;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (h >= num_kv_heads) return;
+  for (int64_t row = blockIdx.x; row < num_tokens; row += gridDim.x) {
+    const int32_t slot = slots[row];
+    if (slot < 0 || slot >= num_blocks * kBlock) continue;  // skipped rows
+    const int64_t blk = slot >> 4, off = slot & 15;
+    const int64_t srow = ((blk * num_kv_heads + h) * kBlock + off);  // scale index; codes at srow * D
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const In* src = (which ? v : k) + (row * num_kv_heads + h) * D + lane * NPL;
+      float x[NPL];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        x[i] = (float)src[i];
+        amax = fmaxf(amax, fabsf(x[i]));
+      }
+      amax = wave_max(amax);
+      const float scale = amax / 448.0f;
+      const float inv = amax != 0.0f ? 448.0f / amax : 0.0f;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const float y = fminf(fmaxf(x[i] * inv, -448.0f), 448.0f);
+        packed |= e4m3_encode(y) << (8 * i);
+      }
+      uint8_t* dst = (which ? v_cache : k_cache) + srow * D + lane * NPL;
+      if constexpr (NPL == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+      } else {
+        *dst = (uint8_t)packed;
+      }
+      if (lane == 0) (which ? v_scale : k_scale)[srow] = scale;
+    }
+  }
+}
+
+hipError_t launch_kv_write_fp8(const WriteArgs& a, int32_t in_dtype, float* k_scale, float* v_scale,
+                               hipStream_t stream) {
+  const int64_t grid64 = a.num_tokens < 65536 ? a.num_tokens : 65536;
+  const dim3 grid((unsigned)grid64, (unsigned)((a.num_kv_heads + 3) / 4)), block(256);
+  auto kc = reinterpret_cast<uint8_t*>(a.k_cache);
+  auto vc = reinterpret_cast<uint8_t*>(a.v_cache);
+  if (in_dtype == 1) {
+    auto k = reinterpret_cast<const __bf16*>(a.k);
+    auto v = reinterpret_cast<const __bf16*>(a.v);
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((kv_write_fp8_kernel<128, __bf16>), grid, block, 0, stream, k, v, a.slots, a.num_tokens, kc,
+                         vc, k_scale, v_scale, a.num_blocks, a.num_kv_heads);
+    else if (a.head_dim == 64)
+      hipLaunchKernelGGL((kv_write_fp8_kernel<64, __bf16>), grid, block, 0, stream, k, v, a.slots, a.num_tokens, kc,
+                         vc, k_scale, v_scale, a.num_blocks, a.num_kv_heads);
+    else
+      return hipErrorInvalidValue;
+  } else if (in_dtype == 0) {
+    auto k = reinterpret_cast<const float*>(a.k);
+    auto v = reinterpret_cast<const float*>(a.v);
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((kv_write_fp8_kernel<128, float>), grid, block, 0, stream, k, v, a.slots, a.num_tokens, kc,
+                         vc, k_scale, v_scale, a.num_blocks, a.num_kv_heads);
+    else if (a.head_dim == 64)
+      hipLaunchKernelGGL((kv_write_fp8_kernel<64, float>), grid, block, 0, stream, k, v, a.slots, a.num_tokens, kc,
+                         vc, k_scale, v_scale, a.num_blocks, a.num_kv_heads);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Copy-on-write: copy whole blocks (every kv head, all 16 slots, K and V).
 // ainews.alishangtian.com article on inference engines, section
 // "PagedAttention": sequences share physical blocks, and a shared block that

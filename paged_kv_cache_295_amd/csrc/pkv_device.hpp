@@ -67,6 +67,7 @@ struct Elem<float> {
     for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(q.w[i]), __uint_as_float(k.w[i]), acc);
     return acc;
   }
+  __device__ __forceinline__ static float dot(const Chunk* q, const Chunk& k, float acc) { return dot(q[0], k, acc); }
   __device__ __forceinline__ static void widen(const Chunk& c, float (&f)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(c.w[i]);
@@ -90,6 +91,7 @@ struct Elem<__bf16> {
                                             __builtin_bit_cast(bf16x2_t, k.w[i]), acc, false);
     return acc;
   }
+  __device__ __forceinline__ static float dot(const Chunk* q, const Chunk& k, float acc) { return dot(q[0], k, acc); }
   __device__ __forceinline__ static void widen(const Chunk& c, float (&f)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -102,6 +104,53 @@ struct Elem<__bf16> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) c.w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     return c;
+  }
+};
+
+// OCP E4M3 cache bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// largest finite 448; no infinities) with one float scale per (slot, kv head):
+// value = e4m3(code) * scale.  Queries and outputs stay bfloat16.
+struct Fp8E4M3 {};
+
+// What a cache element type implies for the decode kernels: the query/output
+// type Q, the bytes per cache element, and whether per-slot scales apply.
+template <typename KV>
+struct KvTraits {
+  using Q = KV;
+  static constexpr int kElemBytes = sizeof(KV);
+  static constexpr bool kScaled = false;
+};
+
+template <>
+struct KvTraits<Fp8E4M3> {
+  using Q = __bf16;
+  static constexpr int kElemBytes = 1;
+  static constexpr bool kScaled = true;
+};
+
+// Two E4M3 codes (bytes 0-1 of w for hi == false, bytes 2-3 for hi == true)
+// widened exactly to a bfloat16 pair (every E4M3 value is a bfloat16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <>
+struct Elem<Fp8E4M3> {
+  static constexpr int kPerChunk = 16;
+  static constexpr int kDtype = 2;
+  // q: the two bfloat16 chunks of the same 16 dims
+  __device__ __forceinline__ static float dot(const Chunk* q, const Chunk& k, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Chunk& qc = q[i >> 1];
+      const int w = (i & 1) * 2;
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qc.w[w]),
+                                            __builtin_bit_cast(bf16x2_t, fp8x2_to_bf16x2<false>(k.w[i])), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qc.w[w + 1]),
+                                            __builtin_bit_cast(bf16x2_t, fp8x2_to_bf16x2<true>(k.w[i])), acc, false);
+    }
+    return acc;
   }
 };
 
@@ -158,9 +207,12 @@ __device__ __forceinline__ float xor_max(float x) {
 }
 
 // All-reduce over the lanes that differ only in the bits >= log2(FROM) of the
-// lane id (the 64 / FROM lane groups of FROM consecutive lanes).
+// lane id (the 64 / FROM lane groups of FROM consecutive lanes), FROM in
+// {4, 8, 16, 32}.  For FROM = 4, ror:4 then ror:8 add the four lanes i, i+4,
+// i+8, i+12 of a row (a cyclic group of rotations).
 template <int FROM>
 __device__ __forceinline__ float groups_add(float x) {
+  if constexpr (FROM <= 4) x += dpp_f32<0x124>(x);  // row_ror:4, then the ror:8 step sums all four
   if constexpr (FROM <= 8) x = xor_add<8>(x);
   if constexpr (FROM <= 16) x = xor_add<16>(x);
   if constexpr (FROM <= 32) x = xor_add<32>(x);
@@ -169,6 +221,7 @@ __device__ __forceinline__ float groups_add(float x) {
 
 template <int FROM>
 __device__ __forceinline__ float groups_max(float x) {
+  if constexpr (FROM <= 4) x = fmaxf(x, dpp_f32<0x124>(x));
   if constexpr (FROM <= 8) x = xor_max<8>(x);
   if constexpr (FROM <= 16) x = xor_max<16>(x);
   if constexpr (FROM <= 32) x = xor_max<32>(x);

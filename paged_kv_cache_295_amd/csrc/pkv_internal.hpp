@@ -56,6 +56,9 @@ struct DecodeArgs {
   const float* init_o;
   const float* init_ml;
   int32_t init_splits;
+  // fp8 caches (dtype 2): float scales [num_blocks][num_kv_heads][16]
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct PrefillArgs {
@@ -87,6 +90,9 @@ struct PrefillArgs {
 };
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+// fp8 caches: quantise bfloat16 (in_dtype 1) or float32 (0) rows to E4M3 codes + per-row scales.
+hipError_t launch_kv_write_fp8(const WriteArgs& a, int32_t in_dtype, float* k_scale, float* v_scale,
+                               hipStream_t stream);
 hipError_t launch_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
                                  int64_t num_pairs, int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
 // Returns hipErrorInvalidValue if no instantiation covers the shape.

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == (1 << 16) | 2
+    assert lib.pkv_abi_version() == (1 << 16) | 3
 
 
 def test_status_strings(lib):
@@ -167,3 +167,39 @@ def test_copy_blocks_validation(lib):
     assert lib.paged_kv_copy_blocks(FAKE, FAKE, ctypes.byref(d), None, FAKE, 3, None) == NULL
     assert lib.paged_kv_copy_blocks(FAKE, FAKE, None, FAKE, FAKE, 3, None) == NULL
     assert lib.paged_kv_copy_blocks(FAKE, FAKE, ctypes.byref(desc(dt=5)), FAKE, FAKE, 3, None) == DTYPE
+
+
+def test_fp8_validation(lib):
+    f8 = desc(dt=2)
+    bf = desc(dt=1)
+    w = lambda d, in_dt=1, k=FAKE, ks=FAKE, T=4: lib.paged_kv_write_fp8(  # noqa: E731
+        k, FAKE, in_dt, FAKE, T, FAKE, FAKE, ks, FAKE, ctypes.byref(d), None)
+    assert w(bf) == DTYPE            # the fp8 writer wants an E4M3 descriptor
+    assert w(f8, in_dt=2) == DTYPE   # and bf16 / f32 rows
+    assert w(f8, ks=None) == NULL
+    assert w(f8, k=None) == NULL
+    assert w(f8, T=-1) == SHAPE
+    assert w(f8, k=None, T=0) == OK
+    assert w(desc(dt=2, d=96)) == UNSUP
+    # the unquantised calls reject an E4M3 cache, the fp8 decode an unquantised one
+    assert write(lib, f8) == DTYPE
+    assert decode(lib, f8) == DTYPE
+
+    def dec8(d, ks=FAKE, vs=FAKE, B=2, hq=32, maxlen=64, ws=FAKE, wsb=1 << 30):
+        return lib.paged_attn_decode_fp8(FAKE, B, hq, FAKE, FAKE, ks, vs, ctypes.byref(d), FAKE, 4, FAKE, maxlen,
+                                         0.1, FAKE, 0, ws, wsb, None)
+    assert dec8(bf) == DTYPE
+    assert dec8(f8, ks=None) == NULL
+    assert dec8(f8, vs=None) == NULL
+    assert dec8(f8, hq=12) == SHAPE
+    assert dec8(f8, maxlen=65) == SHAPE
+    assert dec8(f8, ws=None, wsb=0) == WS
+    assert dec8(f8, B=0) == OK
+    cp = lambda d, ks=FAKE, n=3: lib.paged_kv_copy_blocks_fp8(FAKE, FAKE, ks, FAKE, ctypes.byref(d), FAKE, FAKE, n,  # noqa: E731
+                                                             None)
+    assert cp(bf) == DTYPE
+    assert cp(f8, ks=None) == NULL
+    assert cp(f8, n=-1) == SHAPE
+    assert cp(f8, n=0) == OK
+    assert lib.paged_attn_prefill_chunk(FAKE, 2, 8, 32, FAKE, FAKE, FAKE, ctypes.byref(f8), FAKE, 4, FAKE, 0.1,
+                                        FAKE, None) == DTYPE

@@ -1,0 +1,188 @@
+"""GPU parity of the fp8 (E4M3) KV cache path against the CPU oracle.
+
+Bar: the quantising write is bit-exact (codes and scales over the whole pool,
+poisoned slots included); the block copy is bit-exact; decode over the
+quantised cache is within 2^-6 * max|V| of the oracle's float64 attention over
+the same dequantised values (the kernel rounds the probabilities and the
+output to bfloat16, 3 * 2^-9 * max|V| at most; the bar leaves a margin).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_295_amd as pkv
+import workloads
+from oracle import fp8_cache as f8
+from tests.gpu_util import empty_like_q, to_dev, torch, values
+from workloads import SeqSpec, build
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def u8(a):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to("cuda:0")
+
+
+def f32(a):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+
+
+def host(x):
+    return x.detach().cpu().numpy()
+
+
+class Fp8Device:
+    def __init__(self, w, pool):
+        self.w = w
+        self.kc, self.vc = u8(pool["k_cache"]), u8(pool["v_cache"])
+        self.ks, self.vs = f32(pool["k_scale"]), f32(pool["v_scale"])
+        dt = w.dtype
+        self.new_k, self.new_v = to_dev(w.new_k, dt), to_dev(w.new_v, dt)
+        self.slots = to_dev(w.slot_mapping, dt)
+        self.tables, self.lens = to_dev(w.block_tables, dt), to_dev(w.context_lens, dt)
+
+
+def q_bf16(w):
+    """The workload's decode queries as bfloat16 bits (float32 workloads are rounded)."""
+    return w.q if w.dtype == "bf16" else workloads.f32_to_bf16_bits(w.q)
+
+
+def check_fp8(got, ref, v_codes, v_scale, tables, lens, hkv, what):
+    """|got - ref| <= 2^-6 * max |V| over the (sequence, kv head)'s context."""
+    B, hq, _ = ref.shape
+    worst = 0.0
+    for s in range(B):
+        L = int(lens[s])
+        nb = -(-L // 16)
+        ids = np.asarray(tables[s][:nb], dtype=np.int64)
+        V = f8.dequantize(v_codes[ids], v_scale[ids]) if L else None  # [nb, Hkv, 16, D]
+        for g in range(hkv):
+            if L:
+                rows = V[:, g].reshape(nb * 16, -1)[:L]
+                vmax = float(np.abs(rows).max())
+            else:
+                vmax = 0.0
+            hs = slice(g * (hq // hkv), (g + 1) * (hq // hkv))
+            err = float(np.abs(got[s, hs] - ref[s, hs]).max())
+            assert err <= 2.0 ** -6 * vmax + 1e-30, f"{what}: seq {s} kv head {g}: err {err} vmax {vmax}"
+            worst = max(worst, err / max(vmax, 1e-30))
+    assert np.isfinite(got).all()
+    say(f"{what}: max err / max|V| = {worst:.3e}")
+
+
+def write_and_decode(w, what, partition_tokens=0):
+    pool = workloads.fp8_pool(w)
+    dev = Fp8Device(w, pool)
+    say(f"[{what}] {w.description}; NB={w.num_blocks}")
+    pkv.paged_kv_write_fp8(dev.new_k, dev.new_v, dev.slots, dev.kc, dev.vc, dev.ks, dev.vs)
+    rk, rv, rks, rvs = f8.kv_write_fp8(pool["k_cache"], pool["v_cache"], pool["k_scale"], pool["v_scale"],
+                                       w.new_k, w.new_v, w.slot_mapping, w.dtype)
+    torch().cuda.synchronize()
+    assert host(dev.kc).tobytes() == rk.tobytes() and host(dev.vc).tobytes() == rv.tobytes(), f"{what}: codes"
+    assert host(dev.ks).view(np.uint32).tobytes() == rks.view(np.uint32).tobytes(), f"{what}: K scales"
+    assert host(dev.vs).view(np.uint32).tobytes() == rvs.view(np.uint32).tobytes(), f"{what}: V scales"
+    say(f"[{what}] fp8 write bit-exact ({len(w.slot_mapping)} rows)")
+    if not w.num_seqs:
+        return
+    qb = q_bf16(w)
+    out = empty_like_q(w.q.shape, "bf16")
+    pkv.paged_attn_decode_fp8(to_dev(qb, "bf16"), dev.kc, dev.vc, dev.ks, dev.vs, dev.tables, dev.lens,
+                              float(w.scale), out, max_context_len=w.max_context_len,
+                              partition_tokens=partition_tokens)
+    torch().cuda.synchronize()
+    ref = f8.decode_fp8(qb, rk, rv, rks, rvs, w.block_tables, w.context_lens, w.scale, "bf16")
+    check_fp8(values(out), ref, rv, rvs, w.block_tables, w.context_lens, w.num_kv_heads, f"[{what}] decode")
+
+
+def small(hq, hkv, d, lens, seed, dtype="bf16", **kw):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return build(f"fp8-{hq}-{hkv}-{d}", seed, dtype, hq, hkv, d, [SeqSpec(L, n_new=1 if L else 0) for L in lens],
+                 rng=rng, **kw)
+
+
+def test_all_codes_decode_exactly():
+    """A one-token context returns that token's V row: every finite code, scale 1,
+    comes back as its exact E4M3 value (checks the hardware widening's format)."""
+    hkv, d = 2, 128
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] + [0, 0], np.uint8)  # 256 entries
+    vc = np.zeros((4, hkv, 16, d), np.uint8)
+    vc[1, :, 0, :] = codes.reshape(hkv, d)
+    kc = np.zeros_like(vc)
+    ks = np.ones((4, hkv, 16), np.float32)
+    vs = np.ones((4, hkv, 16), np.float32)
+    q = np.zeros((1, 8, d), np.uint16)
+    out = empty_like_q((1, 8, d), "bf16")
+    pkv.paged_attn_decode_fp8(to_dev(q, "bf16"), u8(kc), u8(vc), f32(ks), f32(vs),
+                              to_dev(np.array([[1]], np.int32), "bf16"), to_dev(np.array([1], np.int32), "bf16"),
+                              1.0, out)
+    torch().cuda.synchronize()
+    got = values(out)[0]
+    for h in range(8):
+        g = h // 4
+        assert np.array_equal(got[h], f8.E4M3_TABLE[codes.reshape(hkv, d)[g]]), f"head {h}"
+
+
+def test_write_ties_and_subnormals_bit_exact():
+    """Rows whose largest magnitude is 448 quantise with inv = 1, so midpoints
+    between codes and subnormal values reach the encoder unchanged."""
+    hkv, d = 1, 128
+    mids = [(f8.E4M3_TABLE[c] + f8.E4M3_TABLE[c + 1]) / 2 for c in range(0, 0x7E)]
+    row = np.array([448.0] + mids + [-mids[5]], np.float32)
+    assert len(row) == d
+    rows = np.stack([row, -row, row * np.float32(0.5), np.zeros(d, np.float32)])[:, None, :]  # [4, 1, 128]
+    bfr = workloads.f32_to_bf16_bits(rows)
+    assert np.array_equal(workloads.bf16_bits_to_f32(bfr), rows)  # exact in bf16
+    kc = np.full((2, hkv, 16, d), 0x7F, np.uint8)
+    ks = np.full((2, hkv, 16), np.nan, np.float32)
+    slots = np.array([0, 17, 31, 5], np.int32)
+    dk, dv, dks, dvs = u8(kc), u8(kc), f32(ks), f32(ks)
+    for in_dtype, data in (("bf16", bfr), ("f32", rows)):
+        pkv.paged_kv_write_fp8(to_dev(data, in_dtype), to_dev(data, in_dtype), to_dev(slots, "bf16"), dk, dv, dks,
+                               dvs)
+        rk, rv, rks, rvs = f8.kv_write_fp8(kc, kc, ks, ks, data, data, slots, in_dtype)
+        torch().cuda.synchronize()
+        assert host(dk).tobytes() == rk.tobytes() and host(dv).tobytes() == rv.tobytes(), in_dtype
+        assert host(dks).view(np.uint32).tobytes() == rks.view(np.uint32).tobytes(), in_dtype
+
+
+FP8_CASES = [
+    (32, 8, 128, [1, 15, 16, 17, 300, 1000, 2049], "bf16"),
+    (64, 8, 128, [5, 600, 33], "bf16"),       # eight heads per wave
+    (8, 8, 64, [3, 100, 257], "bf16"),        # one head per wave, 4 lanes per token
+    (16, 4, 64, [40, 16, 1], "f32"),          # float32 rows quantised
+    (12, 4, 128, [0, 200, 7], "bf16"),        # an empty context, three heads per group
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: f"{c[0]}q{c[1]}kv{c[2]}-{c[4]}-{len(c[3])}seqs")
+@pytest.mark.parametrize("part", [0, 256])
+def test_fp8_write_decode_parity(case, part):
+    hq, hkv, d, lens, dtype = case
+    w = small(hq, hkv, d, lens, seed=hq + d + len(lens), dtype=dtype)
+    write_and_decode(w, f"fp8 {case} part {part}", partition_tokens=part)
+
+
+def test_fp8_llama3_8b_decode():
+    """The Llama-3-8B-shaped decode batch (64 sequences, L ~ U{128..4096})."""
+    write_and_decode(workloads.make(2), "fp8 llama3-8b decode")
+
+
+def test_fp8_copy_blocks_bit_exact():
+    w = small(32, 8, 128, [300, 40], seed=5, num_blocks=64)
+    pool = workloads.fp8_pool(w)
+    dev = Fp8Device(w, pool)
+    src = np.array([3, 9, 70, 12], np.int32)
+    dst = np.array([40, 41, 42, -1], np.int32)
+    pkv.paged_kv_copy_blocks_fp8(to_dev(src, "bf16"), to_dev(dst, "bf16"), dev.kc, dev.vc, dev.ks, dev.vs)
+    torch().cuda.synchronize()
+    rk, rv = oracle.copy_blocks(pool["k_cache"], pool["v_cache"], src, dst)
+    rks, rvs = oracle.copy_blocks(pool["k_scale"][..., None], pool["v_scale"][..., None], src, dst)
+    assert host(dev.kc).tobytes() == rk.tobytes() and host(dev.vc).tobytes() == rv.tobytes()
+    assert host(dev.ks).view(np.uint32).tobytes() == rks[..., 0].view(np.uint32).tobytes()
+    assert host(dev.vs).view(np.uint32).tobytes() == rvs[..., 0].view(np.uint32).tobytes()

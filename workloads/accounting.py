@@ -22,17 +22,20 @@ def kv_ledger_bytes(layers: int, batch: int, kv_heads: int, seq_len: int, head_d
 
 
 def decode_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                 elem_bytes: int, block_tables=None, dedupe_shared: bool = False) -> dict:
+                 elem_bytes: int, block_tables=None, dedupe_shared: bool = False, q_bytes: int = None,
+                 scale_bytes: int = 0) -> dict:
     """Algorithmic bytes of one decode call.
 
     kv:     every (sequence, token) K and V row, or, with dedupe_shared, every
             distinct physical slot once (a prefix shared by many block tables is
-            read once);
-    qo:     the queries read and the outputs written;
+            read once); a quantised cache adds its per-(slot, kv head) K and V
+            scales (scale_bytes each);
+    qo:     the queries read and the outputs written (q_bytes per element,
+            default elem_bytes);
     tables: the block-table entries read and the context lengths.
     """
     lens = np.asarray(context_lens, dtype=np.int64)
-    row = num_kv_heads * head_dim * 2 * elem_bytes  # K + V bytes per token
+    row = num_kv_heads * (head_dim * elem_bytes + scale_bytes) * 2  # K + V bytes per token
     if dedupe_shared:
         assert block_tables is not None
         slots = set()
@@ -45,7 +48,7 @@ def decode_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: in
         kv = len(slots) * row
     else:
         kv = int(lens.sum()) * row
-    qo = 2 * len(lens) * num_q_heads * head_dim * elem_bytes
+    qo = 2 * len(lens) * num_q_heads * head_dim * (elem_bytes if q_bytes is None else q_bytes)
     tables = int(sum(-(-int(L) // BLOCK_SIZE) for L in lens)) * 4 + 4 * len(lens)
     return {"kv": kv, "qo": qo, "tables": tables, "total": kv + qo + tables}
 

@@ -286,6 +286,30 @@ def build(
     )
 
 
+def fp8_pool(w: Workload, seed: Optional[int] = None) -> dict:
+    """An fp8 (E4M3) version of workload w's cache pool, drawn afresh.
+
+    Codes are uniform over the 254 finite E4M3 bytes (0x7F and 0xFF, the NaN
+    codes, excluded) and scales uniform in [2^-12, 2^-6) as float32, one per
+    (slot, kv head).  Slots that w poisons with NaN (no context has reached
+    them) get the NaN code 0x7F and a NaN scale.  Returns uint8 caches
+    [NB, Hkv, 16, D] and float32 scales [NB, Hkv, 16] for K and for V.
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed + 7000 if seed is None else seed))
+    shape = w.k_cache.shape
+    out = {}
+    for name, ref in (("k", w.k_cache), ("v", w.v_cache)):
+        r = rng.integers(0, 254, size=shape, dtype=np.uint8)
+        codes = r + (r >= 0x7F).astype(np.uint8)  # skip 0x7F; the top draw 253 maps to 0xFE
+        scales = rng.uniform(2.0 ** -12, 2.0 ** -6, size=shape[:3]).astype(np.float32)
+        raw = ref[:, :, :, 0]
+        poisoned = (raw == BF16_NAN) if w.dtype == "bf16" else np.isnan(raw)
+        codes[poisoned] = 0x7F
+        scales[poisoned] = np.nan
+        out[name + "_cache"], out[name + "_scale"] = codes, scales
+    return out
+
+
 # --------------------------------------------------------------------------
 # The five serving mixes.  Integer ranges are inclusive.
 
