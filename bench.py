@@ -63,6 +63,7 @@ WORKLOADS = {
     "shared-prefix": 4,
     "long-context": 5,
     "spec-verify": "spec-verify",  # supplementary: speculative-decoding verify (5-row chunks)
+    "spec-verify-b8": "spec-verify-b8",  # the same with 8 sequences (keys split over the GPU)
 }
 
 
@@ -165,8 +166,17 @@ def main():
             pkv.paged_attn_decode(q, kc, vc, tables, lens, scale, out, max_context_len=w.max_context_len,
                                   partition_tokens=part, workspace=ws)
 
+    verify = w.num_seqs == 0 and has_chunks  # the speculative-verify pass: chunk rows only
+    if verify:
+        vws = torch.empty(max(1, pkv.spec_verify_workspace_bytes(w.num_chunks, w.q_chunk.shape[1], w.num_q_heads,
+                                                                w.num_kv_heads, w.head_dim, w.chunk_tables.shape[1])),
+                          dtype=torch.uint8, device=dev)
+
     def prefill():
-        pkv.paged_attn_prefill_chunk(qc, cstart, kc, vc, ctables, clens, scale, oc)
+        if verify:
+            pkv.paged_attn_spec_verify(qc, cstart, kc, vc, ctables, clens, scale, oc, workspace=vws)
+        else:
+            pkv.paged_attn_prefill_chunk(qc, cstart, kc, vc, ctables, clens, scale, oc)
 
     def step():
         write()
@@ -217,7 +227,6 @@ def main():
         ms_per_step = max(ms_per_step - flush_ms, 1e-6)
 
     eb = w.elem_bytes
-    verify = w.num_seqs == 0 and has_chunks  # the verify pass: chunk rows only
     if verify:
         pb = accounting.prefill_bytes(w.chunk_start, w.chunk_context_lens, w.num_q_heads, w.num_kv_heads,
                                       w.head_dim, eb)
@@ -239,7 +248,8 @@ def main():
         traffic = tr["read_bytes"] + tr["write_bytes"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "paged_attn_prefill_chunk: prefill_mfma_kernel" if verify else
+                "kernel": "paged_attn_spec_verify: prefill_mfma_kernel<split> + prefill_split_merge_kernel"
+                if verify else
                           ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
                            "decode_balanced_kernel + decode_balanced_merge_kernel") if cascade else
                           ("paged_attn_decode_fp8: decode_balanced_kernel<fp8> + decode_balanced_merge_kernel"
@@ -259,7 +269,8 @@ def main():
                    "block_size": 16, "num_blocks": w.num_blocks,
                    "context_tokens": int((w.chunk_context_lens if verify else w.context_lens).sum()),
                    "max_context_len": w.max_context_len,
-                   "split": "one workgroup per (chunk, kv head)" if verify else
+                   "split": ("keys of each (sequence, kv head) cut into pieces" if w.num_chunks * w.num_kv_heads < 256
+                             else "one workgroup per (sequence, kv head)") if verify else
                             f"fixed partitions of {part} tokens" if part else
                             (f"shared prefix of {len(w.shared_blocks) * 16} tokens attended once, then " if cascade
                              else "") +

@@ -71,6 +71,57 @@ size_t prefix_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
   return (size_t)ps.splits * num_seqs * num_q_heads * ((size_t)head_dim + 2) * sizeof(float);
 }
 
+// Speculative verify: when the batch has few (sequence, kv head) pairs, cut
+// each row tile's keys into pieces so that the matrix-core kernel still gets
+// about kVerifyWorkgroups workgroups (two per compute unit: the kernel's LDS
+// ring admits one at a time, the second hides the first's start and end).
+// Measured on the MI355X (5 rows per sequence, contexts U{128..4096}): 4 / 8 /
+// 16 sequences take 23 / 45 / 68 us split against 76 / 84 / 101 us unsplit;
+// with 64 sequences x 8 kv heads (512 pairs already) cutting further only
+// added per-workgroup cost: 183 us unsplit, 217 us and 237 us for 1024 and
+// 2048 workgroups.  Pieces are whole 64-key
+// tiles and at least 256 keys, so the partials stay a small fraction of the
+// K/V bytes.
+#ifndef PKV_VERIFY_WORKGROUPS
+#define PKV_VERIFY_WORKGROUPS 512
+#endif
+constexpr int64_t kVerifyWorkgroups = PKV_VERIFY_WORKGROUPS;
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+struct VerifySplit {
+  int32_t splits;  // 1: no split
+  int32_t split_tokens;
+};
+
+VerifySplit verify_split(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t max_blocks_per_seq) {
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t QT = 128 / G;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * ((rows_max + QT - 1) / QT);
+  const int64_t max_keys = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
+  int64_t split = (units * max_keys + kVerifyWorkgroups - 1) / kVerifyWorkgroups;
+  split = (split + 63) / 64 * 64;
+  if (split < 256) split = 256;
+  VerifySplit v;
+  // with a pair per compute unit already, pieces cost more than they balance
+  // (32 sequences x 8 kv heads: 105 us unsplit, 115 us in two pieces)
+  if (units >= kComputeUnits || split >= max_keys) {
+    v.splits = 1;
+    v.split_tokens = 0;
+  } else {
+    v.splits = (int32_t)((max_keys + split - 1) / split);
+    v.split_tokens = (int32_t)split;
+  }
+  return v;
+}
+
+size_t verify_workspace(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_blocks_per_seq) {
+  const VerifySplit v = verify_split(num_seqs, rows_max, num_q_heads, num_kv_heads, max_blocks_per_seq);
+  if (v.splits <= 1) return 0;
+  return (size_t)v.splits * num_seqs * rows_max * num_q_heads * ((size_t)head_dim + 2) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -380,6 +431,46 @@ int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t ch
   a.max_parts = 1;
   a.scale_log2 = sl2;
   return from_hip(launch_decode(a, as_stream(hip_stream)));
+}
+
+size_t paged_attn_spec_verify_workspace_bytes(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
+  if (num_seqs <= 0 || rows_max <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 128)
+    return 0;
+  return verify_workspace(num_seqs, rows_max, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+}
+
+int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
+                           const int32_t* row_start, const void* k_cache, const void* v_cache,
+                           const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !row_start || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (rows_max <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  if (cache->dtype != PKV_DTYPE_BF16 || num_q_heads / cache->num_kv_heads > 128)
+    return paged_attn_prefill_chunk(q, num_seqs, rows_max, num_q_heads, row_start, k_cache, v_cache, cache,
+                                    block_tables, max_blocks_per_seq, context_lens, scale, out, hip_stream);
+  const VerifySplit v = verify_split(num_seqs, rows_max, num_q_heads, cache->num_kv_heads, max_blocks_per_seq);
+  const size_t need = verify_workspace(num_seqs, rows_max, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                       max_blocks_per_seq);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  PrefillArgs a{q, out, k_cache, v_cache, block_tables, context_lens, row_start, num_seqs, rows_max, num_q_heads,
+                cache->num_kv_heads, cache->head_dim, cache->num_blocks, max_blocks_per_seq, scale * kLog2eHost};
+  if (v.splits > 1) {
+    a.split_tokens = v.split_tokens;
+    a.num_splits = v.splits;
+    a.part_o = reinterpret_cast<float*>(workspace);
+    a.part_ml = a.part_o + (size_t)v.splits * num_seqs * rows_max * num_q_heads * cache->head_dim;
+  }
+  return from_hip(launch_prefill_mfma(a, as_stream(hip_stream)));
 }
 
 }  // extern "C"

@@ -138,12 +138,18 @@ __device__ __forceinline__ void wait_vmcnt_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
 }
 
-// PREFIX = false: chunked prefill (rows = chunk rows x G heads of one kv head,
-// keys 0 .. row position, causal).  PREFIX = true: the shared prefix of a
+// MODE kChunk: chunked prefill (rows = chunk rows x G heads of one kv head,
+// keys 0 .. row position, causal).  MODE kPrefix: the shared prefix of a
 // batch of decode queries (rows = (sequence, head) pairs of one kv head, keys
 // = one piece of the prefix, no causal mask), written as (m, l, o) partials.
-template <int D, bool PREFIX>
+// MODE kSplit: chunked prefill with each row tile's keys cut into pieces of
+// split_tokens, one workgroup per piece; a row tile with one piece writes its
+// output, the others write (m, l, o) partials for prefill_split_merge_kernel.
+constexpr int kChunk = 0, kPrefix = 1, kSplit = 2;
+
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables) {
+  constexpr bool PREFIX = MODE == kPrefix;
   using S = PrefillShape<D>;
   constexpr int NS = S::kNS;
   constexpr int RC = S::kRC;
@@ -164,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
 
   int c, g, kt0, kend, ntiles, nblk, mask_from, qpos, head;
   bool row_ok;
+  bool partial = PREFIX;  // write (m, l, o) partials instead of the output
   const __bf16* qrow;
   int64_t part_row = 0;  // PREFIX: (piece, sequence, head) row of the partials
   int64_t out_row = 0;   // prefill: (chunk, row) of q and out
@@ -190,8 +197,13 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
     const int QT = kMRows / G;
     const int n_mt = (a.chunk_len_max + QT - 1) / QT;
     const int npair = a.num_chunks * a.num_kv_heads;
-    const int pair = id % npair;
-    const int mt = n_mt - 1 - id / npair;  // the longest row tiles start first
+    int t = id, sp = 0;
+    if constexpr (MODE == kSplit) {  // the pieces of a row tile are consecutive workgroups
+      sp = t % a.num_splits;
+      t /= a.num_splits;
+    }
+    const int pair = t % npair;
+    const int mt = n_mt - 1 - t / npair;  // the longest row tiles start first
     c = pair / a.num_kv_heads;
     g = pair - c * a.num_kv_heads;
 
@@ -201,6 +213,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
     const bool bad_chunk = P0 < 0 || n < 0 || L > a.max_blocks_per_seq * kBlock || n > a.chunk_len_max;
     const int row0 = mt * QT;
     if (bad_chunk) {
+      if (sp != 0) return;  // piece 0 writes the NaN rows
       const int rows = min(QT, a.chunk_len_max - row0);
       for (int idx = tid; idx < rows * G * D; idx += kThreads) {
         const int r = idx / (G * D), rem = idx - r * G * D;
@@ -213,15 +226,26 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
     if (rows_here <= 0) return;
     kend = P0 + row0 + rows_here;  // keys [0, kend) are visible to some row
     kt0 = 0;
-    ntiles = (kend + kKT - 1) / kKT;
-    nblk = (kend + kBlock - 1) / kBlock;  // table entries that are read
-    mask_from = P0 + row0 + 1;            // the first key some row may not see
+    mask_from = P0 + row0 + 1;  // the first key some row may not see
     const int hl = mrow / QT;
     const int qi = row0 + (mrow - hl * QT);
-    row_ok = hl < G && qi < n;
     qpos = P0 + qi;
+    if constexpr (MODE == kSplit) {
+      const int k0 = sp * a.split_tokens;  // a multiple of the key tile
+      if (k0 >= kend) return;             // no keys left for this piece
+      partial = kend > a.split_tokens;    // more than one piece: partials
+      kt0 = k0 / kKT;
+      kend = min(kend, k0 + a.split_tokens);
+      // keys of later pieces are masked like keys past the row's position
+      mask_from = min(mask_from, kend);
+      qpos = min(qpos, kend - 1);
+    }
+    ntiles = (kend + kKT - 1) / kKT;
+    nblk = (kend + kBlock - 1) / kBlock;  // table entries that are read
+    row_ok = hl < G && qi < n;
     head = g * G + hl;
     out_row = (int64_t)c * a.chunk_len_max + qi;
+    part_row = (((int64_t)sp * a.num_chunks + c) * a.chunk_len_max + qi) * a.num_q_heads + head;
     qrow = reinterpret_cast<const __bf16*>(a.q) + (out_row * a.num_q_heads + head) * D;
   }
 
@@ -438,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
   const int any_bad = __syncthreads_or(local_bad);
   const float l_tot = l_run + shfl_xor_f32(l_run, 32);
   if (!row_ok) return;
-  if constexpr (PREFIX) {
+  if (partial) {
     float* po = a.part_o + part_row * D;
 #pragma unroll
     for (int nd = 0; nd < S::kND; ++nd)
@@ -452,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
       a.part_ml[part_row * 2] = any_bad ? __builtin_nanf("") : m_run;
       a.part_ml[part_row * 2 + 1] = l_tot;
     }
-  } else {
+  } else if constexpr (!PREFIX) {
     const float inv = any_bad ? __builtin_nanf("") : 1.0f / l_tot;
     __bf16* orow = out + (out_row * a.num_q_heads + head) * D;
 #pragma unroll
@@ -468,26 +492,90 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(const PrefillArg
   }
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
+// Merge of the key pieces of every split row tile: one wave per (chunk, row,
+// head) row whose tile was cut into more than one piece; lane k owns dims
+// k, k + 64, ...  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M the
+// largest m_p; a NaN m_p (contract broken) makes the row NaN.
+template <int D>
+__global__ __launch_bounds__(64) void prefill_split_merge_kernel(const PrefillArgs a) {
+  constexpr int PER = D / kWave;
+  const int lane = __lane_id();
+  const int64_t item = blockIdx.x;  // (chunk, row, head)
+  const int head = (int)(item % a.num_q_heads);
+  const int64_t cr = item / a.num_q_heads;
+  const int c = (int)(cr / a.chunk_len_max);
+  const int qi = (int)(cr - (int64_t)c * a.chunk_len_max);
   const int G = a.num_q_heads / a.num_kv_heads;
-  if (G < 1 || G > kMRows) return hipErrorInvalidValue;
   const int QT = kMRows / G;
-  const int64_t n_mt = (a.chunk_len_max + QT - 1) / QT;
-  const int64_t grid = n_mt * a.num_chunks * a.num_kv_heads;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int P0 = a.chunk_start[c];
+  const int L = a.context_lens[c];
+  const int n = L - P0;
+  if (P0 < 0 || n < 0 || L > a.max_blocks_per_seq * kBlock || n > a.chunk_len_max || qi >= n) return;
+  const int row0 = qi / QT * QT;
+  const int kend = P0 + row0 + min(QT, n - row0);
+  if (kend <= a.split_tokens) return;  // one piece: written by the main kernel
+  const int np = (kend + a.split_tokens - 1) / a.split_tokens;
+  const int64_t stride = (int64_t)a.num_chunks * a.chunk_len_max * a.num_q_heads;  // rows per piece
+  float M = -__builtin_inff();
+  bool nan = false;
+  for (int p = 0; p < np; ++p) {
+    const float m = a.part_ml[(p * stride + item) * 2];
+    nan |= m != m;
+    M = fmaxf(M, m);
+  }
+  float lam = 0.0f, o[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+  for (int p = 0; p < np; ++p) {
+    const int64_t r = p * stride + item;
+    const float f = fast_exp2(a.part_ml[r * 2] - M);
+    lam = fmaf(f, a.part_ml[r * 2 + 1], lam);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = fmaf(f, a.part_o[r * D + lane + e * kWave], o[e]);
+  }
+  const float inv = nan ? __builtin_nanf("") : 1.0f / lam;
+  __bf16* orow = reinterpret_cast<__bf16*>(a.out) + item * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) orow[lane + e * kWave] = (__bf16)(o[e] * inv);
+}
+
+template <int MODE>
+static hipError_t launch_chunk_modes(const PrefillArgs& a, int64_t grid, hipStream_t stream) {
   switch (a.head_dim) {
     case 64:
-      hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+      hipLaunchKernelGGL((prefill_mfma_kernel<64, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
                          a.block_tables);
       break;
     case 128:
-      hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+      hipLaunchKernelGGL((prefill_mfma_kernel<128, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
                          a.block_tables);
       break;
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (G < 1 || G > kMRows) return hipErrorInvalidValue;
+  const int QT = kMRows / G;
+  const int64_t n_mt = (a.chunk_len_max + QT - 1) / QT;
+  const bool split = a.num_splits > 1;
+  if (split && (a.split_tokens <= 0 || a.split_tokens % kKT != 0 || !a.part_o || !a.part_ml))
+    return hipErrorInvalidValue;
+  const int64_t grid = n_mt * a.num_chunks * a.num_kv_heads * (split ? a.num_splits : 1);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (!split) return launch_chunk_modes<kChunk>(a, grid, stream);
+  hipError_t e = launch_chunk_modes<kSplit>(a, grid, stream);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.num_chunks * a.chunk_len_max * a.num_q_heads;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(prefill_split_merge_kernel<64>, dim3((unsigned)rows), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_split_merge_kernel<128>, dim3((unsigned)rows), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -498,19 +586,7 @@ hipError_t launch_prefix_mfma(const PrefillArgs& a, hipStream_t stream) {
   const int64_t grid = n_mt * a.num_kv_heads * a.num_splits;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  switch (a.head_dim) {
-    case 64:
-      hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
-                         a.block_tables);
-      break;
-    case 128:
-      hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
-                         a.block_tables);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_chunk_modes<kPrefix>(a, grid, stream);
 }
 
 }  // namespace pkv

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == (1 << 16) | 3
+    assert lib.pkv_abi_version() == (1 << 16) | 4
 
 
 def test_status_strings(lib):
@@ -203,3 +203,24 @@ def test_fp8_validation(lib):
     assert cp(f8, n=0) == OK
     assert lib.paged_attn_prefill_chunk(FAKE, 2, 8, 32, FAKE, FAKE, FAKE, ctypes.byref(f8), FAKE, 4, FAKE, 0.1,
                                         FAKE, None) == DTYPE
+
+
+def test_spec_verify_validation_and_workspace(lib):
+    d = desc()
+    v = lambda q=FAKE, B=64, R=5, hq=32, maxb=257, ws=FAKE, wsb=1 << 30, dd=d: lib.paged_attn_spec_verify(  # noqa: E731
+        q, B, R, hq, FAKE, FAKE, FAKE, ctypes.byref(dd), FAKE, maxb, FAKE, 0.1, FAKE, ws, wsb, None)
+    assert v(B=0, q=None) == OK
+    assert v(q=None) == NULL
+    assert v(R=0) == SHAPE
+    assert v(hq=20) == SHAPE
+    assert v(B=8, ws=None, wsb=0) == WS
+    assert v(dd=desc(dt=2)) == DTYPE
+    # 64 sequences x 8 kv heads: enough workgroups, no split and no workspace
+    assert lib.paged_attn_spec_verify_workspace_bytes(64, 5, 32, 8, 128, 257) == 0
+    # 8 sequences x 8 kv heads of 5 rows, 257 blocks: pieces of 576 keys, 8 per row tile
+    need = lib.paged_attn_spec_verify_workspace_bytes(8, 5, 32, 8, 128, 257)
+    assert need == 8 * 8 * 5 * 32 * 130 * 4
+    assert v(B=8, wsb=need - 1) == WS
+    # one piece covers the table: no workspace
+    assert lib.paged_attn_spec_verify_workspace_bytes(2, 5, 32, 8, 128, 16) == 0
+    assert lib.paged_attn_spec_verify_workspace_bytes(2, 5, 12, 8, 128, 16) == 0

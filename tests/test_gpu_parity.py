@@ -272,6 +272,7 @@ def test_prefill_chunk_parity(case):
 # speculative-decoding verify: many sequences with k + 1 = 2..9 causal rows each
 VERIFY_CASES = [
     ("bf16", 32, 8, 128, 5, 40, 11),
+    ("bf16", 32, 8, 128, 5, 64, 16),
     ("bf16", 64, 8, 128, 3, 24, 12),
     ("bf16", 32, 8, 128, 9, 16, 13),
     ("bf16", 8, 8, 64, 2, 30, 14),
@@ -279,18 +280,67 @@ VERIFY_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", VERIFY_CASES, ids=lambda c: f"{c[0]}-{c[1]}q{c[2]}kv-{c[3]}d-rows{c[4]}-{c[5]}seqs")
-def test_spec_verify_parity(case):
-    """Each sequence verifies up to k drafts: a chunk of 1..k+1 rows (ragged: some
-    sequences accepted fewer) over contexts from a few tokens to a few thousand."""
+def verify_workload(case):
     dtype, hq, hkv, d, rows, nseq, seed = case
     rng = np.random.default_rng(seed)
     ctx = rng.integers(1, 3000, size=nseq)
     ctx[:3] = [0, 15, 16]  # empty context, a ragged block, an exact block
     n = rng.integers(1, rows + 1, size=nseq)
     n[:2] = rows
-    w = chunk_workload(dtype, hq, hkv, d, list(zip(ctx.tolist(), n.tolist())), seed=seed, cmax=rows)
-    write_decode_prefill_vs_oracle(w, f"verify {case}")
+    return chunk_workload(dtype, hq, hkv, d, list(zip(ctx.tolist(), n.tolist())), seed=seed, cmax=rows)
+
+
+def run_verify(dw):
+    w = dw.w
+    out = empty_like_q(w.q_chunk.shape, w.dtype, fill_nan=False)
+    out.fill_(SENTINEL)
+    need = pkv.spec_verify_workspace_bytes(w.num_chunks, w.q_chunk.shape[1], w.num_q_heads, w.num_kv_heads,
+                                           w.head_dim, w.chunk_tables.shape[1])
+    ws = torch().full((max(need, 1),), 0xFF, dtype=torch().uint8, device=device())  # NaN-filled workspace
+    pkv.paged_attn_spec_verify(dw.q_chunk, dw.chunk_start, dw.k_cache, dw.v_cache, dw.chunk_tables, dw.chunk_lens,
+                               float(w.scale), out, workspace=ws)
+    torch().cuda.synchronize()
+    return out, need
+
+
+@pytest.mark.parametrize("case", VERIFY_CASES, ids=lambda c: f"{c[0]}-{c[1]}q{c[2]}kv-{c[3]}d-rows{c[4]}-{c[5]}seqs")
+def test_spec_verify_parity(case):
+    """Each sequence verifies up to k drafts: a chunk of 1..k+1 rows (ragged: some
+    sequences accepted fewer) over contexts from a few tokens to a few thousand,
+    through the prefill-chunk call and through the verify call (keys split)."""
+    w = verify_workload(case)
+    dw, rk, rv = write_decode_prefill_vs_oracle(w, f"verify {case}")
+    out, need = run_verify(dw)
+    say(f"verify call: workspace {need} bytes")
+    ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale,
+                               w.dtype)
+    got = values(out)
+    for c in range(w.num_chunks):
+        n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+        check_attn(got[c, :n], ref[c, :n], w.dtype, f"verify call, sequence {c}")
+        assert (got[c, n:] == SENTINEL).all(), "rows past the sequence's count must not be written"
+
+
+def test_spec_verify_split_bad_sequence_gives_nan():
+    """A sequence that breaks the contract (more rows than rows_max) gets NaN rows;
+    the others are unaffected, with the keys split into pieces."""
+    case = ("bf16", 32, 8, 128, 4, 24, 21)
+    w = verify_workload(case)
+    good_start = w.chunk_start.copy()
+    w.chunk_start[5] = w.chunk_context_lens[5] - 6  # 6 rows > rows_max 4
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    out, need = run_verify(dw)
+    assert need > 0
+    ref = oracle.prefill_chunk(w.q_chunk, good_start, ref_k, ref_v, w.chunk_tables, w.chunk_context_lens,
+                               w.scale, w.dtype)
+    got = values(out)
+    for c in range(w.num_chunks):
+        if c == 5:
+            assert np.isnan(got[c]).all()
+            continue
+        n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+        check_attn(got[c, :n], ref[c, :n], w.dtype, f"sequence {c}")
 
 
 def test_prefill_last_row_equals_decode():

@@ -379,7 +379,7 @@ def spec_verify(seed: Optional[int] = None, batch: int = 64, k: int = 4, lo: int
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = rng.integers(lo, hi + 1, size=batch)
     seqs = [SeqSpec(int(L) + k, n_new=k + 1, kind="chunk") for L in lens]
-    return build(f"spec-verify-k{k}-bf16", seed, "bf16", 32, 8, 128, seqs, max_blocks_chunk=-(-(hi + k) // BLOCK_SIZE),
+    return build(f"spec-verify-k{k}-bf16" if batch == 64 else f"spec-verify-k{k}-b{batch}-bf16", seed, "bf16", 32, 8, 128, seqs, max_blocks_chunk=-(-(hi + k) // BLOCK_SIZE),
                  chunk_len_max=k + 1, rng=rng,
                  description=f"{batch} seqs, accepted L~U{{{lo}..{hi}}} + {k} drafts ({k + 1} causal rows each), "
                              "32q/8kv x 128, bf16")
@@ -397,6 +397,7 @@ CONFIGS = {
 # Supplementary workloads for the rows beyond the five mixes, by name.
 SUPPLEMENTARY = {
     "spec-verify": spec_verify,
+    "spec-verify-b8": lambda seed=None: spec_verify(seed, batch=8),
 }
 
 
