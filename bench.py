@@ -37,22 +37,26 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 # HBM traffic of one decode call, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch summed over the call's two
 # kernels), scaled by what the same counters read for a device copy of 256 MiB
-# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel sources it was
-# measured on: reported as null once their hash differs.
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by (workload, --kv-dtype).  Valid
+# only for the decode kernel sources it was measured on: reported as null once
+# their hash differs.
 TRAFFIC = {
-    "llama3-8b-decode-bf16": {"read_bytes": 520879186, "write_bytes": 3421872,
-                              "sources_sha256": "dd62faad531789dd2682e21c8c6a2f84d374151a94eec810d61689fc4776bded"},
+    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 520526643, "write_bytes": 3422003,
+                                        "sources_sha256": "bd104d296e7795e0a4093d589eae43c24c2f94cbf799c0058ac0051372673a26"},
+    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 279003546, "write_bytes": 3419648,
+                                      "sources_sha256": "bd104d296e7795e0a4093d589eae43c24c2f94cbf799c0058ac0051372673a26"},
 }
 CSRC = os.path.join(ROOT, "paged_kv_cache_295_amd", "csrc")
+DECODE_SOURCES = ("decode.hip", "pkv_device.hpp", "pkv_internal.hpp")
 
 
 def sources_sha256() -> str:
+    """Hash of the sources the decode kernels are built from."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in DECODE_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -242,9 +246,9 @@ def main():
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     seq_tok_s = n_seq / (ms_per_step * 1e-3)
     achieved = dec["total"] / (launch_ms * 1e-3) / 1e9 if launch_ms > 0 else 0.0
-    tr = TRAFFIC.get(w.name)
+    tr = TRAFFIC.get((w.name, args.kv_dtype))
     traffic = None
-    if tr is not None and tr["sources_sha256"] == sources_sha256() and part == 0 and not args.cold and not fp8:
+    if tr is not None and tr["sources_sha256"] == sources_sha256() and part == 0 and not args.cold and not verify:
         traffic = tr["read_bytes"] + tr["write_bytes"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
