@@ -42,8 +42,15 @@ size_t partition_workspace(int32_t num_seqs, int32_t hq, int32_t head_dim, int32
   return (size_t)num_seqs * hq * max_parts * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-// Shared prefix: pieces of the prefix for the matrix-core kernel, enough to give
-// each of the 256 compute units about one workgroup (128 rows x 64-key tiles).
+// Workgroups of the matrix-core kernel the MI355X runs at once: two per
+// compute unit on 256 compute units (its LDS ring and registers admit two).
+#ifndef PKV_MATRIX_SLOTS
+#define PKV_MATRIX_SLOTS 512
+#endif
+constexpr int64_t kMatrixSlots = PKV_MATRIX_SLOTS;
+
+// Shared prefix: pieces of the prefix for the matrix-core kernel, enough to
+// fill every workgroup slot about once (128 rows x 64-key tiles each).
 struct PrefixSplit {
   int32_t splits;
   int32_t split_tokens;
@@ -54,7 +61,7 @@ PrefixSplit prefix_split(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_h
   const int64_t row_tiles = (num_seqs * G + 127) / 128;
   const int64_t wgs = row_tiles * num_kv_heads;
   const int64_t tiles = (prefix_len + 63) / 64;
-  int64_t want = (256 + wgs - 1) / wgs;
+  int64_t want = (kMatrixSlots + wgs - 1) / wgs;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   const int64_t per = (tiles + want - 1) / want;
@@ -71,22 +78,17 @@ size_t prefix_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
   return (size_t)ps.splits * num_seqs * num_q_heads * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-// Speculative verify: when the batch has few (sequence, kv head) pairs, cut
-// each row tile's keys into pieces so that the matrix-core kernel still gets
-// about kVerifyWorkgroups workgroups (two per compute unit: the kernel's LDS
-// ring admits one at a time, the second hides the first's start and end).
-// Measured on the MI355X (5 rows per sequence, contexts U{128..4096}): 4 / 8 /
-// 16 sequences take 23 / 45 / 68 us split against 76 / 84 / 101 us unsplit;
-// with 64 sequences x 8 kv heads (512 pairs already) cutting further only
-// added per-workgroup cost: 183 us unsplit, 217 us and 237 us for 1024 and
-// 2048 workgroups.  Pieces are whole 64-key
-// tiles and at least 256 keys, so the partials stay a small fraction of the
-// K/V bytes.
-#ifndef PKV_VERIFY_WORKGROUPS
-#define PKV_VERIFY_WORKGROUPS 512
-#endif
-constexpr int64_t kVerifyWorkgroups = PKV_VERIFY_WORKGROUPS;
-constexpr int64_t kComputeUnits = 256;  // MI355X
+// Speculative verify: when the batch has fewer (sequence, kv head) pairs than
+// workgroup slots, cut each row tile's keys into pieces so that the matrix-
+// core kernel gets about two workgroups per slot, the second wave of them
+// hiding the first's start and end.  Measured on the MI355X (5 rows per
+// sequence, contexts U{128..4096}, one workgroup per compute unit at the
+// time): 4 / 8 / 16 sequences took 23 / 45 / 68 us split against 76 / 84 /
+// 101 us unsplit; with every slot already holding a pair, cutting further only
+// added per-workgroup cost (64 sequences x 8 kv heads: 183 us unsplit, 217 us
+// and 237 us for 1024 and 2048 workgroups).  Pieces are whole 64-key tiles and
+// at least 256 keys, so the partials stay a small fraction of the K/V bytes.
+constexpr int64_t kVerifyWorkgroups = 2 * kMatrixSlots;
 
 struct VerifySplit {
   int32_t splits;  // 1: no split
@@ -103,9 +105,8 @@ VerifySplit verify_split(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads
   split = (split + 63) / 64 * 64;
   if (split < 256) split = 256;
   VerifySplit v;
-  // with a pair per compute unit already, pieces cost more than they balance
-  // (32 sequences x 8 kv heads: 105 us unsplit, 115 us in two pieces)
-  if (units >= kComputeUnits || split >= max_keys) {
+  // with a pair per slot already, pieces cost more than they balance
+  if (units >= kMatrixSlots || split >= max_keys) {
     v.splits = 1;
     v.split_tokens = 0;
   } else {

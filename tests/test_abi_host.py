@@ -215,11 +215,12 @@ def test_spec_verify_validation_and_workspace(lib):
     assert v(hq=20) == SHAPE
     assert v(B=8, ws=None, wsb=0) == WS
     assert v(dd=desc(dt=2)) == DTYPE
-    # 64 sequences x 8 kv heads: enough workgroups, no split and no workspace
+    # 64 sequences x 8 kv heads: a pair for every workgroup slot, no split and no workspace
     assert lib.paged_attn_spec_verify_workspace_bytes(64, 5, 32, 8, 128, 257) == 0
-    # 8 sequences x 8 kv heads of 5 rows, 257 blocks: pieces of 576 keys, 8 per row tile
+    # 8 sequences x 8 kv heads of 5 rows, 257 blocks: 64 pairs for 512 workgroup slots, pieces
+    # of ceil(64 * 4112 / 1024) = 257 -> 320 keys (whole tiles), 13 per row tile
     need = lib.paged_attn_spec_verify_workspace_bytes(8, 5, 32, 8, 128, 257)
-    assert need == 8 * 8 * 5 * 32 * 130 * 4
+    assert need == 13 * 8 * 5 * 32 * 130 * 4
     assert v(B=8, wsb=need - 1) == WS
     # one piece covers the table: no workspace
     assert lib.paged_attn_spec_verify_workspace_bytes(2, 5, 32, 8, 128, 16) == 0
