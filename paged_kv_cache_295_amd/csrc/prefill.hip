@@ -88,6 +88,14 @@ struct PrefillShape {
   static_assert((kNS - 2) * kDW < 64, "vmcnt is six bits");
 };
 
+// Chunk rows per row tile: a tile holds 128 (head, row) pairs of one kv head.
+// When all of a chunk's rows for the G heads fit one tile (short chunks: the
+// speculative-verify rows), they are packed densely -- head-major, chunk_len_max
+// rows per head -- so the waves past them carry no query and skip the math.
+__host__ __device__ __forceinline__ int tile_rows(int chunk_len_max, int G) {
+  return chunk_len_max * G <= kMRows ? chunk_len_max : kMRows / G;
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   uint4 u = make_uint4(a, b, c, d);
   return __builtin_bit_cast(bf16x8_t, u);
@@ -206,7 +214,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     qrow = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)(row_ok ? seq : 0) * a.num_q_heads + head) * D;
     part_row = ((int64_t)sp * a.num_chunks + seq) * a.num_q_heads + head;
   } else {
-    const int QT = kMRows / G;
+    const int QT = tile_rows(a.chunk_len_max, G);
     const int n_mt = (a.chunk_len_max + QT - 1) / QT;
     const int npair = a.num_chunks * a.num_kv_heads;
     int t = id, sp = 0;
@@ -355,6 +363,9 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     issue(kt0 + t, p);
   }
 
+  // a wave whose 32 rows carry no query only loads and synchronises
+  const bool wave_active = __builtin_amdgcn_ballot_w64(row_ok) != 0;
+
   // Tile kt: wait for its loads, start the loads of tile kt + NS - 1, then
   // S^T = K Q^T, the online softmax and O^T += V^T P^T.  MASK: the tile holds
   // keys past some row's position (diagonal tiles; the last one also holds
@@ -382,6 +393,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       }
     }
+    if (!wave_active) return;
 
     f32x16_t st[2];
     {
@@ -518,7 +530,7 @@ __global__ __launch_bounds__(64) void prefill_split_merge_kernel(const PrefillAr
   const int c = (int)(cr / a.chunk_len_max);
   const int qi = (int)(cr - (int64_t)c * a.chunk_len_max);
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int QT = kMRows / G;
+  const int QT = tile_rows(a.chunk_len_max, G);
   const int P0 = a.chunk_start[c];
   const int L = a.context_lens[c];
   const int n = L - P0;
@@ -571,7 +583,7 @@ static hipError_t launch_chunk_modes(const PrefillArgs& a, int64_t grid, hipStre
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   if (G < 1 || G > kMRows) return hipErrorInvalidValue;
-  const int QT = kMRows / G;
+  const int QT = tile_rows(a.chunk_len_max, G);
   const int64_t n_mt = (a.chunk_len_max + QT - 1) / QT;
   const bool split = a.num_splits > 1;
   if (split && (a.split_tokens <= 0 || a.split_tokens % kKT != 0 || !a.part_o || !a.part_ml))
