@@ -154,21 +154,26 @@ struct PV<Fp8E4M3, NP, CPL, GB> {
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
+          for (int w = 0; w < 4; ++w) {
+            // interleave the codes of the two tokens (byte permute: token p's bytes
+            // are selectors 0-3, token p+1's 4-7), so that each widening of a byte
+            // pair yields (token p, token p+1) of one dim, the operand order of P
+            const uint32_t a0 = vv[p][c].w[w], a1 = vv[p + 1][c].w[w];
+            const uint32_t lo = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // dims 4w, 4w+1
+            const uint32_t hi = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // dims 4w+2, 4w+3
+            const bf16x2_t d0 = __builtin_bit_cast(bf16x2_t, fp8x2_to_bf16x2<false>(lo));
+            const bf16x2_t d1 = __builtin_bit_cast(bf16x2_t, fp8x2_to_bf16x2<true>(lo));
+            const bf16x2_t d2 = __builtin_bit_cast(bf16x2_t, fp8x2_to_bf16x2<false>(hi));
+            const bf16x2_t d3 = __builtin_bit_cast(bf16x2_t, fp8x2_to_bf16x2<true>(hi));
+            const int e = 4 * w;
 #pragma unroll
-            for (int hi = 0; hi < 2; ++hi) {  // dims 4w + 2hi, 4w + 2hi + 1
-              const uint32_t a0 = hi ? fp8x2_to_bf16x2<true>(vv[p][c].w[w]) : fp8x2_to_bf16x2<false>(vv[p][c].w[w]);
-              const uint32_t a1 =
-                  hi ? fp8x2_to_bf16x2<true>(vv[p + 1][c].w[w]) : fp8x2_to_bf16x2<false>(vv[p + 1][c].w[w]);
-              const bf16x2_t ev = __builtin_bit_cast(bf16x2_t, (a0 & 0xffffu) | (a1 << 16));
-              const bf16x2_t od = __builtin_bit_cast(bf16x2_t, (a0 >> 16) | (a1 & 0xffff0000u));
-              const int e = 4 * w + 2 * hi;
-#pragma unroll
-              for (int h = 0; h < GB; ++h) {
-                acc[h][c][e] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], ev, acc[h][c][e], false);
-                acc[h][c][e + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], od, acc[h][c][e + 1], false);
-              }
+            for (int h = 0; h < GB; ++h) {
+              acc[h][c][e] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], d0, acc[h][c][e], false);
+              acc[h][c][e + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], d1, acc[h][c][e + 1], false);
+              acc[h][c][e + 2] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], d2, acc[h][c][e + 2], false);
+              acc[h][c][e + 3] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], d3, acc[h][c][e + 3], false);
             }
+          }
       }
     } else {  // one token per lane per block: widened values, plain FMAs
 #pragma unroll
@@ -314,7 +319,9 @@ struct Segment {
   }
 
   // Attend the query rows over one tile whose first token (of this lane's
-  // pass 0) is tok0; tokens at or past `end` are masked.
+  // pass 0) is tok0; tokens at or past `end` are masked.  (A branch to a
+  // select-free variant for whole blocks was measured slower: the two code
+  // paths cost the register pipeline its fixed placement.)
   __device__ __forceinline__ void compute(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
                                           const float (&sk)[NSC], const float (&sv)[NSC], int tok0, int end) {
     float x[NP * GB];
