@@ -176,11 +176,17 @@ def main():
                                                                 w.num_kv_heads, w.head_dim, w.chunk_tables.shape[1])),
                           dtype=torch.uint8, device=dev)
 
+    elif has_chunks:
+        pws = torch.empty(max(1, pkv.prefill_chunk_workspace_bytes(w.num_chunks, w.q_chunk.shape[1], w.num_q_heads,
+                                                                  w.num_kv_heads, w.head_dim,
+                                                                  w.chunk_tables.shape[1])),
+                          dtype=torch.uint8, device=dev)
+
     def prefill():
         if verify:
             pkv.paged_attn_spec_verify(qc, cstart, kc, vc, ctables, clens, scale, oc, workspace=vws)
         else:
-            pkv.paged_attn_prefill_chunk(qc, cstart, kc, vc, ctables, clens, scale, oc)
+            pkv.paged_attn_prefill_chunk_ws(qc, cstart, kc, vc, ctables, clens, scale, oc, workspace=pws)
 
     def step():
         write()

@@ -314,6 +314,25 @@ int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t ch
 
 /* Human-readable name of a status code (static storage). */
 /*
+ * paged_attn_prefill_chunk_ws -- paged_attn_prefill_chunk with a workspace:
+ * the same arguments, result and device-side contract, and a caller-owned
+ * device workspace of at least paged_attn_prefill_chunk_workspace_bytes(...)
+ * bytes (0 means none is needed: the call then behaves as the plain one).
+ * When the batch has fewer (chunk, row tile, kv head) units than the GPU runs
+ * workgroups at once, the keys of every row tile are cut into pieces spread
+ * over the GPU and combined by a log-sum-exp merge, so one long row tile does
+ * not run alone at the end.  bfloat16 runs on the matrix cores; float32 takes
+ * the plain call's path (no workspace used).
+ */
+size_t paged_attn_prefill_chunk_workspace_bytes(int32_t num_chunks, int32_t chunk_len_max, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq);
+int paged_attn_prefill_chunk_ws(const void* q_chunk, int32_t num_chunks, int32_t chunk_len_max, int32_t num_q_heads,
+                                const int32_t* chunk_start, const void* k_cache, const void* v_cache,
+                                const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, float scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
+
+/*
  * paged_attn_spec_verify -- the target model's attention pass that verifies
  * speculative draft tokens.  (Serving deep-dive page, paragraph on
  * speculative decoding, and the caffein.top essay, section "Speculative
@@ -323,13 +342,11 @@ int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t ch
  * i at position row_start[s] + i attends causally to keys 0 .. that position:
  * exactly paged_attn_prefill_chunk's result with chunk_len_max = rows_max
  * (same argument layout and device-side contract, rows past a sequence's
- * count not written).  What differs is the work split: the rows of a sequence
- * are few and the contexts long and ragged, so each (sequence, kv head)'s keys
- * are cut into pieces spread over the whole GPU, and a log-sum-exp merge
- * combines the pieces.  That needs a workspace of at least
- * paged_attn_spec_verify_workspace_bytes(...) bytes (0: none needed, for
- * example when one piece covers 16 * max_blocks_per_seq keys).  bfloat16
- * caches run on the matrix cores; float32 caches take the prefill-chunk path.
+ * count not written), computed as by paged_attn_prefill_chunk_ws: the rows of
+ * a sequence are few, so they share one row tile per kv head, and with few
+ * sequences each (sequence, kv head)'s keys are cut into pieces spread over
+ * the GPU.  Workspace: at least paged_attn_spec_verify_workspace_bytes(...)
+ * bytes (0: none needed).
  */
 size_t paged_attn_spec_verify_workspace_bytes(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq);
@@ -343,7 +360,7 @@ const char* pkv_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION ((1 << 16) | 4)
+#define PKV_ABI_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,8 @@ __all__ = [
     "decode_workspace_bytes", "decode_split_waves", "library_path", "BLOCK_SIZE",
     "paged_attn_decode_shared_prefix", "shared_prefix_workspace_bytes", "paged_kv_copy_blocks", "BlockPool",
     "paged_kv_write_fp8", "paged_attn_decode_fp8", "paged_kv_copy_blocks_fp8",
-    "paged_attn_spec_verify", "spec_verify_workspace_bytes",
+    "paged_attn_spec_verify", "spec_verify_workspace_bytes", "paged_attn_prefill_chunk_ws",
+    "prefill_chunk_workspace_bytes",
 ]
 
 BLOCK_SIZE = 16
@@ -90,6 +91,10 @@ def load_library():
     lib.paged_block_append_slot.restype = ctypes.c_int
     lib.paged_block_release.argtypes = [ip, i32, ip, i32, ip, ip]
     lib.paged_block_release.restype = ctypes.c_int
+    lib.paged_attn_prefill_chunk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attn_prefill_chunk_workspace_bytes.restype = sz
+    lib.paged_attn_prefill_chunk_ws.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp, sz, vp]
+    lib.paged_attn_prefill_chunk_ws.restype = ctypes.c_int
     lib.paged_attn_spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_attn_spec_verify_workspace_bytes.restype = sz
     lib.paged_attn_spec_verify.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp, sz, vp]
@@ -406,15 +411,19 @@ class BlockPool:
                "paged_block_release")
 
 
+def prefill_chunk_workspace_bytes(num_chunks, chunk_len_max, num_q_heads, num_kv_heads, head_dim,
+                                  max_blocks_per_seq) -> int:
+    return int(load_library().paged_attn_prefill_chunk_workspace_bytes(num_chunks, chunk_len_max, num_q_heads,
+                                                                       num_kv_heads, head_dim, max_blocks_per_seq))
+
+
 def spec_verify_workspace_bytes(num_seqs, rows_max, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq) -> int:
     return int(load_library().paged_attn_spec_verify_workspace_bytes(num_seqs, rows_max, num_q_heads, num_kv_heads,
                                                                      head_dim, max_blocks_per_seq))
 
 
-def paged_attn_spec_verify(q, row_start, k_cache, v_cache, block_tables, context_lens, scale, out, workspace=None,
-                           stream=None):
-    """Verify pass of speculative decoding: q [B, R, Hq, D] holds each sequence's new rows
-    (last accepted token + drafts) at positions row_start[s] + i; causal attention over the cache."""
+def _chunks_with_workspace(fn, size_fn, what, q, starts, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           workspace, stream):
     lib = load_library()
     torch = _torch()
     _same_dtype(q, out, k_cache, v_cache)
@@ -422,17 +431,34 @@ def paged_attn_spec_verify(q, row_start, k_cache, v_cache, block_tables, context
     nb_, rows, hq, d = q.shape
     if out.shape != q.shape or d != desc.head_dim:
         raise ValueError("q/out must be [B, rows, Hq, head_dim]")
-    if block_tables.dim() != 2 or block_tables.shape[0] != nb_ or row_start.shape != (nb_,) \
+    if block_tables.dim() != 2 or block_tables.shape[0] != nb_ or starts.shape != (nb_,) \
             or context_lens.shape != (nb_,):
-        raise ValueError("block_tables [B, max_blocks], row_start [B], context_lens [B]")
-    need = spec_verify_workspace_bytes(nb_, rows, hq, desc.num_kv_heads, d, block_tables.shape[1])
+        raise ValueError("block_tables [B, max_blocks], starts [B], context_lens [B]")
+    need = size_fn(nb_, rows, hq, desc.num_kv_heads, d, block_tables.shape[1])
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.paged_attn_spec_verify(_ptr(q), nb_, rows, hq, _i32(row_start, "row_start"), _ptr(k_cache),
-                                    _ptr(v_cache), ctypes.byref(desc), _i32(block_tables, "block_tables"),
-                                    block_tables.shape[1], _i32(context_lens, "context_lens"), float(scale), _ptr(out),
-                                    ws_ptr, ws_bytes, _stream(stream))
-    _check(st, "paged_attn_spec_verify")
+    st = getattr(lib, fn)(_ptr(q), nb_, rows, hq, _i32(starts, "starts"), _ptr(k_cache), _ptr(v_cache),
+                          ctypes.byref(desc), _i32(block_tables, "block_tables"), block_tables.shape[1],
+                          _i32(context_lens, "context_lens"), float(scale), _ptr(out), ws_ptr, ws_bytes,
+                          _stream(stream))
+    _check(st, what)
     return out
+
+
+def paged_attn_prefill_chunk_ws(q_chunk, chunk_start, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                workspace=None, stream=None):
+    """paged_attn_prefill_chunk with a workspace, which lets the keys of long row tiles be split over the GPU."""
+    return _chunks_with_workspace("paged_attn_prefill_chunk_ws", prefill_chunk_workspace_bytes,
+                                  "paged_attn_prefill_chunk_ws", q_chunk, chunk_start, k_cache, v_cache,
+                                  block_tables, context_lens, scale, out, workspace, stream)
+
+
+def paged_attn_spec_verify(q, row_start, k_cache, v_cache, block_tables, context_lens, scale, out, workspace=None,
+                           stream=None):
+    """Verify pass of speculative decoding: q [B, R, Hq, D] holds each sequence's new rows
+    (last accepted token + drafts) at positions row_start[s] + i; causal attention over the cache."""
+    return _chunks_with_workspace("paged_attn_spec_verify", spec_verify_workspace_bytes, "paged_attn_spec_verify",
+                                  q, row_start, k_cache, v_cache, block_tables, context_lens, scale, out, workspace,
+                                  stream)

@@ -78,35 +78,40 @@ size_t prefix_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
   return (size_t)ps.splits * num_seqs * num_q_heads * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-// Speculative verify: when the batch has fewer (sequence, kv head) pairs than
-// workgroup slots, cut each row tile's keys into pieces so that the matrix-
-// core kernel gets about two workgroups per slot, the second wave of them
-// hiding the first's start and end.  Measured on the MI355X (5 rows per
+// Chunks with a workspace (prefill chunks, the speculative-verify rows): when
+// the batch has fewer (chunk, row tile, kv head) units than workgroup slots,
+// cut each row tile's keys into pieces so that the matrix-core kernel gets
+// about two workgroups per slot, the second wave of them hiding the first's
+// start and end, and no long row tile runs alone at the end.  Measured on the MI355X (5 rows per
 // sequence, contexts U{128..4096}, one workgroup per compute unit at the
 // time): 4 / 8 / 16 sequences took 23 / 45 / 68 us split against 76 / 84 /
 // 101 us unsplit; with every slot already holding a pair, cutting further only
 // added per-workgroup cost (64 sequences x 8 kv heads: 183 us unsplit, 217 us
 // and 237 us for 1024 and 2048 workgroups).  Pieces are whole 64-key tiles and
 // at least 256 keys, so the partials stay a small fraction of the K/V bytes.
-constexpr int64_t kVerifyWorkgroups = 2 * kMatrixSlots;
+constexpr int64_t kChunkWorkgroups = 2 * kMatrixSlots;
 
-struct VerifySplit {
+struct ChunkSplit {
   int32_t splits;  // 1: no split
   int32_t split_tokens;
 };
 
-VerifySplit verify_split(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t max_blocks_per_seq) {
+ChunkSplit chunk_split(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t max_blocks_per_seq) {
   const int64_t G = num_q_heads / num_kv_heads;
-  const int64_t QT = 128 / G;
+  const int64_t QT = (int64_t)rows_max * G <= 128 ? rows_max : 128 / G;  // rows per tile, as the kernel packs them
   const int64_t units = (int64_t)num_seqs * num_kv_heads * ((rows_max + QT - 1) / QT);
   const int64_t max_keys = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
-  int64_t split = (units * max_keys + kVerifyWorkgroups - 1) / kVerifyWorkgroups;
+  int64_t split = (units * max_keys + kChunkWorkgroups - 1) / kChunkWorkgroups;
   split = (split + 63) / 64 * 64;
   if (split < 256) split = 256;
-  VerifySplit v;
-  // with a pair per slot already, pieces cost more than they balance
-  if (units >= kMatrixSlots || split >= max_keys) {
+  ChunkSplit v;
+  // with a unit for every other slot already, pieces cost more than they
+  // balance: the mixed-step chunks (2 x 512 rows, 256 units) take 52 us
+  // unsplit against 78 us in pieces of 1024 keys plus a 14 us merge, while one
+  // 512-row chunk at 3584 keys (128 units) takes 95 us unsplit, 58 + 18 us in
+  // pieces of 512
+  if (2 * units >= kMatrixSlots || split >= max_keys) {
     v.splits = 1;
     v.split_tokens = 0;
   } else {
@@ -116,9 +121,9 @@ VerifySplit verify_split(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads
   return v;
 }
 
-size_t verify_workspace(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t max_blocks_per_seq) {
-  const VerifySplit v = verify_split(num_seqs, rows_max, num_q_heads, num_kv_heads, max_blocks_per_seq);
+size_t chunk_workspace(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t max_blocks_per_seq) {
+  const ChunkSplit v = chunk_split(num_seqs, rows_max, num_q_heads, num_kv_heads, max_blocks_per_seq);
   if (v.splits <= 1) return 0;
   return (size_t)v.splits * num_seqs * rows_max * num_q_heads * ((size_t)head_dim + 2) * sizeof(float);
 }
@@ -434,12 +439,52 @@ int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t ch
   return from_hip(launch_decode(a, as_stream(hip_stream)));
 }
 
-size_t paged_attn_spec_verify_workspace_bytes(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
-                                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
-  if (num_seqs <= 0 || rows_max <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+size_t paged_attn_prefill_chunk_workspace_bytes(int32_t num_chunks, int32_t chunk_len_max, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
+  if (num_chunks <= 0 || chunk_len_max <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 128)
     return 0;
-  return verify_workspace(num_seqs, rows_max, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+  return chunk_workspace(num_chunks, chunk_len_max, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+}
+
+int paged_attn_prefill_chunk_ws(const void* q_chunk, int32_t num_chunks, int32_t chunk_len_max, int32_t num_q_heads,
+                                const int32_t* chunk_start, const void* k_cache, const void* v_cache,
+                                const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, float scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* hip_stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_chunks < 0) return PKV_ERR_SHAPE;
+  if (num_chunks == 0) return PKV_OK;
+  if (!q_chunk || !chunk_start || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return PKV_ERR_NULL;
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (chunk_len_max <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  if (cache->dtype != PKV_DTYPE_BF16 || num_q_heads / cache->num_kv_heads > 128)
+    return paged_attn_prefill_chunk(q_chunk, num_chunks, chunk_len_max, num_q_heads, chunk_start, k_cache, v_cache,
+                                    cache, block_tables, max_blocks_per_seq, context_lens, scale, out, hip_stream);
+  const ChunkSplit v = chunk_split(num_chunks, chunk_len_max, num_q_heads, cache->num_kv_heads, max_blocks_per_seq);
+  const size_t need = chunk_workspace(num_chunks, chunk_len_max, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                      max_blocks_per_seq);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  PrefillArgs a{q_chunk, out, k_cache, v_cache, block_tables, context_lens, chunk_start, num_chunks, chunk_len_max,
+                num_q_heads, cache->num_kv_heads, cache->head_dim, cache->num_blocks, max_blocks_per_seq,
+                scale * kLog2eHost};
+  if (v.splits > 1) {
+    a.split_tokens = v.split_tokens;
+    a.num_splits = v.splits;
+    a.part_o = reinterpret_cast<float*>(workspace);
+    a.part_ml = a.part_o + (size_t)v.splits * num_chunks * chunk_len_max * num_q_heads * cache->head_dim;
+  }
+  return from_hip(launch_prefill_mfma(a, as_stream(hip_stream)));
+}
+
+size_t paged_attn_spec_verify_workspace_bytes(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
+  return paged_attn_prefill_chunk_workspace_bytes(num_seqs, rows_max, num_q_heads, num_kv_heads, head_dim,
+                                                  max_blocks_per_seq);
 }
 
 int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
@@ -447,31 +492,9 @@ int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, in
                            const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, float scale, void* out, void* workspace,
                            size_t workspace_bytes, void* hip_stream) {
-  int st = check_cache(cache);
-  if (st != PKV_OK) return st;
-  if (num_seqs < 0) return PKV_ERR_SHAPE;
-  if (num_seqs == 0) return PKV_OK;
-  if (!q || !row_start || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
-  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
-  if (rows_max <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
-  if (!isfinite(scale)) return PKV_ERR_SHAPE;
-  if (cache->dtype != PKV_DTYPE_BF16 || num_q_heads / cache->num_kv_heads > 128)
-    return paged_attn_prefill_chunk(q, num_seqs, rows_max, num_q_heads, row_start, k_cache, v_cache, cache,
-                                    block_tables, max_blocks_per_seq, context_lens, scale, out, hip_stream);
-  const VerifySplit v = verify_split(num_seqs, rows_max, num_q_heads, cache->num_kv_heads, max_blocks_per_seq);
-  const size_t need = verify_workspace(num_seqs, rows_max, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                       max_blocks_per_seq);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-  PrefillArgs a{q, out, k_cache, v_cache, block_tables, context_lens, row_start, num_seqs, rows_max, num_q_heads,
-                cache->num_kv_heads, cache->head_dim, cache->num_blocks, max_blocks_per_seq, scale * kLog2eHost};
-  if (v.splits > 1) {
-    a.split_tokens = v.split_tokens;
-    a.num_splits = v.splits;
-    a.part_o = reinterpret_cast<float*>(workspace);
-    a.part_ml = a.part_o + (size_t)v.splits * num_seqs * rows_max * num_q_heads * cache->head_dim;
-  }
-  return from_hip(launch_prefill_mfma(a, as_stream(hip_stream)));
+  return paged_attn_prefill_chunk_ws(q, num_seqs, rows_max, num_q_heads, row_start, k_cache, v_cache, cache,
+                                     block_tables, max_blocks_per_seq, context_lens, scale, out, workspace,
+                                     workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == (1 << 16) | 4
+    assert lib.pkv_abi_version() == (1 << 16) | 5
 
 
 def test_status_strings(lib):
@@ -225,3 +225,20 @@ def test_spec_verify_validation_and_workspace(lib):
     # one piece covers the table: no workspace
     assert lib.paged_attn_spec_verify_workspace_bytes(2, 5, 32, 8, 128, 16) == 0
     assert lib.paged_attn_spec_verify_workspace_bytes(2, 5, 12, 8, 128, 16) == 0
+
+
+def test_prefill_chunk_ws_workspace(lib):
+    # the mixed-step chunks: 2 chunks x 512 rows, 32q/8kv: 2 x 16 row tiles x 8 kv heads = 256 units, a unit
+    # for every other slot of 512: no split
+    assert lib.paged_attn_prefill_chunk_workspace_bytes(2, 512, 32, 8, 128, 256) == 0
+    # one such chunk: 128 units, 256 blocks -> pieces of ceil(128 * 4096 / 1024) = 512 keys, 8 per row tile
+    assert lib.paged_attn_prefill_chunk_workspace_bytes(1, 512, 32, 8, 128, 256) == 8 * 1 * 512 * 32 * 130 * 4
+    # 16 chunks x 512 rows: 2048 units, every slot busy: no split
+    assert lib.paged_attn_prefill_chunk_workspace_bytes(16, 512, 32, 8, 128, 256) == 0
+    d = desc()
+    c = lambda ws=FAKE, wsb=1 << 30, n=1: lib.paged_attn_prefill_chunk_ws(  # noqa: E731
+        FAKE, n, 512, 32, FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, 256, FAKE, 0.1, FAKE, ws, wsb, None)
+    assert c(ws=None, wsb=0) == WS
+    assert c(n=0) == OK
+    assert lib.paged_attn_spec_verify_workspace_bytes(8, 5, 32, 8, 128, 257) == \
+        lib.paged_attn_prefill_chunk_workspace_bytes(8, 5, 32, 8, 128, 257)

@@ -343,6 +343,34 @@ def test_spec_verify_split_bad_sequence_gives_nan():
         check_attn(got[c, :n], ref[c, :n], w.dtype, f"sequence {c}")
 
 
+WS_CASES = PREFILL_CASES[:6] + [("bf16", 32, 8, 128, [(1000, 300)]),       # 80 units: keys split
+                                 ("bf16", 64, 8, 128, [(2000, 100), (0, 5)])]  # split, and a chunk in one piece
+
+
+@pytest.mark.parametrize("case", WS_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}-{c[3]}-{len(c[4])}ch")
+def test_prefill_chunk_ws_parity(case):
+    """The workspace variant (row tiles' keys split over the GPU when units are few)."""
+    dtype, hq, hkv, d, chunks = case
+    w = chunk_workload(dtype, hq, hkv, d, chunks, seed=11, cmax=max(n for _, n in chunks) + 3)
+    dw = DeviceWorkload(w)
+    rk, rv = run_write(dw)
+    out = empty_like_q(w.q_chunk.shape, w.dtype, fill_nan=False)
+    out.fill_(SENTINEL)
+    need = pkv.prefill_chunk_workspace_bytes(w.num_chunks, w.q_chunk.shape[1], hq, hkv, d, w.chunk_tables.shape[1])
+    ws = torch().full((max(need, 1),), 0xFF, dtype=torch().uint8, device=device())
+    pkv.paged_attn_prefill_chunk_ws(dw.q_chunk, dw.chunk_start, dw.k_cache, dw.v_cache, dw.chunk_tables,
+                                    dw.chunk_lens, float(w.scale), out, workspace=ws)
+    torch().cuda.synchronize()
+    say(f"prefill_chunk_ws {case}: workspace {need} bytes")
+    ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale,
+                               w.dtype)
+    got = values(out)
+    for c in range(w.num_chunks):
+        n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+        check_attn(got[c, :n], ref[c, :n], w.dtype, f"chunk {c}")
+        assert (got[c, n:] == SENTINEL).all()
+
+
 def test_prefill_last_row_equals_decode():
     """The last row of a chunk is the decode query of the same position."""
     w = chunk_workload("bf16", 32, 8, 128, [(300, 200)], seed=12)
