@@ -926,23 +926,10 @@ __global__ __launch_bounds__(64) void prefix_merge_kernel(float* __restrict__ pa
   const int lane = __lane_id();
   const int64_t row = blockIdx.x;
   if (row >= rows) return;
-  float M = -__builtin_inff();
-  bool nan = false;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float m = part_ml[(sp * rows + row) * 2];
-    nan |= m != m;
-    M = fmaxf(M, m);
-  }
-  float lam = 0.0f, o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const int64_t r = sp * rows + row;
-    const float f = fast_exp2(part_ml[r * 2] - M);
-    lam = fmaf(f, part_ml[r * 2 + 1], lam);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = fmaf(f, part_o[r * D + lane + e * kWave], o[e]);
-  }
+  float M, lam, o[PER];
+  bool nan;
+  merge_partials<D>(part_o, part_ml, row, rows, splits, o, M, lam, nan);
+  // the wave has read every partial (piece 0 included) before it overwrites piece 0
 #pragma unroll
   for (int e = 0; e < PER; ++e) part_o[row * D + lane + e * kWave] = o[e];
   if (lane == 0) {

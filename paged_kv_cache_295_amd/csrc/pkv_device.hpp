@@ -247,6 +247,48 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Log-sum-exp merge of n partial states of one row, partial p at row index
+// row0 + p * stride of part_ml (m in log2 units, l) and part_o (D floats,
+// unnormalised).  Lane p loads partial p's (m, l), so every load is in flight
+// at once; lane k ends with dims k, k + 64, ... of sum_p 2^(m_p - M) o_p in o
+// and every lane with lam = sum_p 2^(m_p - M) l_p and M = max_p m_p.  nan:
+// some m_p is NaN (the partial's inputs broke the contract).
+template <int D>
+__device__ __forceinline__ void merge_partials(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                               int64_t row0, int64_t stride, int n, float (&o)[D / kWave],
+                                               float& M, float& lam, bool& nan) {
+  constexpr int PER = D / kWave;
+  const int lane = __lane_id();
+  M = -__builtin_inff();
+  nan = false;
+  for (int p0 = 0; p0 < n; p0 += kWave) {
+    const int p = p0 + lane;
+    const float m = p < n ? part_ml[(row0 + p * stride) * 2] : -__builtin_inff();
+    nan |= __builtin_amdgcn_ballot_w64(m != m) != 0;
+    M = fmaxf(M, wave_max(m));
+  }
+  lam = 0.0f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+  for (int p0 = 0; p0 < n; p0 += kWave) {
+    const int p = p0 + lane;
+    float f = 0.0f, l = 0.0f;
+    if (p < n) {
+      f = fast_exp2(part_ml[(row0 + p * stride) * 2] - M);
+      l = part_ml[(row0 + p * stride) * 2 + 1];
+    }
+    lam += wave_sum(f * l);
+    const int cnt = min(kWave, n - p0);
+#pragma unroll 4
+    for (int j = 0; j < cnt; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+      const float* src = part_o + (row0 + (int64_t)(p0 + j) * stride) * D + lane;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = fmaf(fj, src[e * kWave], o[e]);
+    }
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ T uniform(T v) {
   return (T)__builtin_amdgcn_readfirstlane((int)v);

@@ -540,23 +540,9 @@ __global__ __launch_bounds__(64) void prefill_split_merge_kernel(const PrefillAr
   if (kend <= a.split_tokens) return;  // one piece: written by the main kernel
   const int np = (kend + a.split_tokens - 1) / a.split_tokens;
   const int64_t stride = (int64_t)a.num_chunks * a.chunk_len_max * a.num_q_heads;  // rows per piece
-  float M = -__builtin_inff();
-  bool nan = false;
-  for (int p = 0; p < np; ++p) {
-    const float m = a.part_ml[(p * stride + item) * 2];
-    nan |= m != m;
-    M = fmaxf(M, m);
-  }
-  float lam = 0.0f, o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.0f;
-  for (int p = 0; p < np; ++p) {
-    const int64_t r = p * stride + item;
-    const float f = fast_exp2(a.part_ml[r * 2] - M);
-    lam = fmaf(f, a.part_ml[r * 2 + 1], lam);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = fmaf(f, a.part_o[r * D + lane + e * kWave], o[e]);
-  }
+  float M, lam, o[PER];
+  bool nan;
+  merge_partials<D>(a.part_o, a.part_ml, item, stride, np, o, M, lam, nan);
   const float inv = nan ? __builtin_nanf("") : 1.0f / lam;
   __bf16* orow = reinterpret_cast<__bf16*>(a.out) + item * D;
 #pragma unroll
