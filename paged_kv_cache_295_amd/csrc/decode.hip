@@ -78,7 +78,11 @@ struct DecodeShape {
   static constexpr int kRowChunks = D / kEPC;           // chunks per token row of one kv head
   static constexpr int kCPL = kRowChunks / LPT;         // chunks per lane per token
   static constexpr int kTPP = kWave / LPT;              // tokens covered by one load pass
-  static constexpr int kNPass = kBlock / kTPP;          // tokens per lane per block
+  static constexpr int kPPB = kBlock / kTPP;            // passes (tokens per lane) per block
+  // Blocks per pipeline tile: two when a block gives a lane a single token, so
+  // that every tile still gives each lane a pair of tokens for the PV product.
+  static constexpr int kBPT = kPPB == 1 ? 2 : 1;
+  static constexpr int kNPass = kPPB * kBPT;            // tokens per lane per tile
   static_assert(kRowChunks % LPT == 0 && kCPL >= 1, "LPT must divide the chunks of a row");
   static_assert(kBlock % kTPP == 0, "a block must be a whole number of passes");
 };
@@ -234,6 +238,9 @@ struct Segment {
   using E = typename S::E;
   using T = typename S::Q;
   static constexpr int EPC = S::kEPC, CPL = S::kCPL, TPP = S::kTPP, NP = S::kNPass, QPC = S::kQPC;
+  static constexpr int PPB = S::kPPB, BPT = S::kBPT;
+  // token (relative to the tile's first token of this lane) of pass p
+  static constexpr int tok_of(int p) { return (p / PPB) * kBlock + (p % PPB) * TPP; }
   static constexpr int RB = S::kRowBytes;
   static constexpr bool kScaled = KvTraits<KV>::kScaled;
   // scales carried per stage (one dummy entry when there are none)
@@ -288,32 +295,34 @@ struct Segment {
     bad_block = false;
   }
 
-  // One K tile and one V tile (16 tokens of one kv head) at byte offset off of
-  // the caches.  Every tile is loaded whole (rows past the context in a last
-  // block are still inside it): one constant per-lane offset plus immediates,
-  // so no address arithmetic sits between the loads of consecutive tiles.
+  // The K and V tiles (16 tokens of one kv head each) of the BPT blocks of a
+  // pipeline tile, block b at byte offset off[b] of the caches.  Every block
+  // is loaded whole (rows past the context in a last block are still inside
+  // it): one constant per-lane offset plus immediates, so no address
+  // arithmetic sits between the loads of consecutive tiles.
   __device__ __forceinline__ void load_tile(Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], float (&sk)[NSC],
-                                            float (&sv)[NSC], int64_t off) const {
+                                            float (&sv)[NSC], const int64_t (&off)[BPT]) const {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const int o = lane_base + p * TPP * RB + c * LPT * 16;
+        const int64_t ob = off[p / PPB];
+        const int o = lane_base + (p % PPB) * TPP * RB + c * LPT * 16;
         if constexpr (kStreamKV) {
-          kk[p][c] = load_chunk_stream(kc + off + o);
-          vv[p][c] = load_chunk_stream(vc + off + o);
+          kk[p][c] = load_chunk_stream(kc + ob + o);
+          vv[p][c] = load_chunk_stream(vc + ob + o);
         } else {
-          kk[p][c] = load_chunk(kc + off + o);
-          vv[p][c] = load_chunk(vc + off + o);
+          kk[p][c] = load_chunk(kc + ob + o);
+          vv[p][c] = load_chunk(vc + ob + o);
         }
       }
     if constexpr (kScaled) {
-      // the tile's 16 scales sit at (block * kv heads + kv head) * 16, i.e. off / RB
-      const int64_t so = off / RB + tg;
+      // a block's 16 scales sit at (block * kv heads + kv head) * 16, i.e. its offset / RB
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        sk[p] = __builtin_nontemporal_load(ksc + so + p * TPP);
-        sv[p] = __builtin_nontemporal_load(vsc + so + p * TPP);
+        const int64_t so = off[p / PPB] / RB + tg + (p % PPB) * TPP;
+        sk[p] = __builtin_nontemporal_load(ksc + so);
+        sv[p] = __builtin_nontemporal_load(vsc + so);
       }
     }
   }
@@ -341,7 +350,7 @@ struct Segment {
       // scaled caches: the token's K scale multiplies its dot products
       const float f = kScaled ? sk[kScaled ? p : 0] * sl2 : sl2;
 #pragma unroll
-      for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + p * TPP < end ? x[p * GB + h] * f : -__builtin_inff();
+      for (int h = 0; h < GB; ++h) sc[p][h] = tok0 + tok_of(p) < end ? x[p * GB + h] * f : -__builtin_inff();
     }
     bool need = false;
     float bm[GB];
@@ -382,7 +391,7 @@ struct Segment {
     Chunk vz[NP][CPL];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const bool ok = tok0 + p * TPP < end;
+      const bool ok = tok0 + tok_of(p) < end;
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -448,38 +457,47 @@ struct Segment {
     };
     auto block_off = [&](int jb) -> int64_t { return tile_off(table[jb]); };
 
-    // NS register stages: while block jb is computed, blocks jb+1 .. jb+NS-1
-    // are in flight and block jb+NS is issued right after.  The prologue fills
-    // every stage so that the loop is entered in its steady state; past the end
-    // loads re-read the last block (an L2 hit), so no load is conditional.  The
-    // body computes NS blocks and exits only at its end (a single exit keeps the
-    // accumulators in place); blocks past the last one lie wholly past `end`,
-    // are masked and add exactly nothing.  Table entries are fetched one pass
-    // ahead.
+    // NS register stages of BPT blocks each: while tile jt is computed, tiles
+    // jt+1 .. jt+NS-1 are in flight and tile jt+NS is issued right after.  The
+    // prologue fills every stage so that the loop is entered in its steady
+    // state; past the end loads re-read the last block (an L2 hit), so no load
+    // is conditional.  The body computes NS tiles and exits only at its end (a
+    // single exit keeps the accumulators in place); blocks past the last one
+    // lie wholly past `end`, are masked and add exactly nothing.  Table entries
+    // are fetched one pass ahead.
+    constexpr int TB = NS * BPT;  // blocks per loop pass
     Chunk kS[NS][NP][CPL], vS[NS][NP][CPL];
     float skS[NS][NSC], svS[NS][NSC];
     const int last = nblk - 1;
-    int64_t offs[NS];
-    int first[2 * NS];  // the first 2 NS entries, fetched together
+    int64_t offs[NS][BPT];
+    int first[2 * TB];  // the first 2 NS tiles' entries, fetched together
 #pragma unroll
-    for (int i = 0; i < 2 * NS; ++i) first[i] = table[min(i, last)];
+    for (int i = 0; i < 2 * TB; ++i) first[i] = table[min(i, last)];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      load_tile(kS[st], vS[st], skS[st], svS[st], tile_off(first[st]));
+      int64_t o[BPT];
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) o[b] = tile_off(first[st * BPT + b]);
+      load_tile(kS[st], vS[st], skS[st], svS[st], o);
       // each stage's loads are issued before the next stage's: waits are in order
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int st = 0; st < NS; ++st) offs[st] = tile_off(first[NS + st]);
-    for (int jb = 0;; jb += NS) {
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) offs[st][b] = tile_off(first[TB + st * BPT + b]);
+    for (int jb = 0;; jb += TB) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        compute(kS[st], vS[st], skS[st], svS[st], (blk0 + jb + st) * kBlock + tg, end);
-        const int64_t next = block_off(min(jb + 2 * NS + st, last));
+        compute(kS[st], vS[st], skS[st], svS[st], (blk0 + jb + st * BPT) * kBlock + tg, end);
+        int64_t next[BPT];
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) next[b] = block_off(min(jb + 2 * TB + st * BPT + b, last));
         load_tile(kS[st], vS[st], skS[st], svS[st], offs[st]);
-        offs[st] = next;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) offs[st][b] = next[b];
       }
-      if (jb + NS >= nblk) break;
+      if (jb + TB >= nblk) break;
     }
   }
 
@@ -963,10 +981,17 @@ hipError_t launch_prefix_merge(float* part_o, float* part_ml, int64_t rows, int 
 #ifndef PKV_DECODE_STAGES
 #define PKV_DECODE_STAGES 2
 #endif
+// fp8 at head_dim 128 keeps 8 lanes per token: 4 (two blocks per pipeline
+// tile, half the replicated softmax work) was measured slower, 72.8 us against
+// 60 us on the Llama-3-8B batch -- the accumulators no longer fit the
+// architectural registers and the token-group merge doubles.
+#ifndef PKV_DECODE_LPT_FP8
+#define PKV_DECODE_LPT_FP8 8
+#endif
 template <typename KV, int D, int GB>
 constexpr int lanes_per_token() {
   constexpr int row_chunks = D * KvTraits<KV>::kElemBytes / 16;
-  constexpr int want = GB >= 8 ? 16 : PKV_DECODE_LPT_SMALL_GROUP;
+  constexpr int want = GB >= 8 ? 16 : (KvTraits<KV>::kScaled ? PKV_DECODE_LPT_FP8 : PKV_DECODE_LPT_SMALL_GROUP);
   return row_chunks < want ? row_chunks : want;
 }
 // Register stages of the K/V prefetch pipeline (fixed partitions).
