@@ -71,6 +71,22 @@ static_assert(kKT == kWaves * 16, "one cache block per wave and tile");
 #ifndef PKV_PREFILL_WAVES_PER_SIMD
 #define PKV_PREFILL_WAVES_PER_SIMD 2
 #endif
+// (A loop with K one tile ahead of V in separate rings, the next tile's
+// scores issued before this tile's softmax, was measured no faster: 54 us
+// against 52.5 us on the mixed-step chunks, 673 us against 658 us for 16 x 512
+// rows at 3584 keys.)
+
+// XOR swizzle of the 16-byte chunks of V row `key` (K rows use key mod chunks);
+// it must repeat every 16 rows (the reads add whole 16-row steps as immediate
+// offsets).  0: key mod chunks; 1: 2 key mod chunks; 2: 4 (key mod 4) +
+// (key / 4) mod 4.  A transpose read serves 32 lanes at a time over 64 banks
+// on gfx950: each 16-lane group reads 4 consecutive keys x 32 bytes, and only
+// option 2 spreads the two groups' 8 key-chunk pairs over distinct banks
+// (rocprofv3 SQ_LDS_BANK_CONFLICT: 95.2 M cycles with option 0, 31.7 M with
+// option 1, 0 with option 2; 16 x 512 rows at 3584 keys 668 -> 644 us).
+#ifndef PKV_PREFILL_VSWZ
+#define PKV_PREFILL_VSWZ 2
+#endif
 
 template <int D>
 struct PrefillShape {
@@ -86,6 +102,11 @@ struct PrefillShape {
   static constexpr int kND = D / 32;                     // PV output blocks of 32 head dims
   static_assert(kRowsPerLoad * kRC == 64, "one load covers whole rows");
   static_assert((kNS - 2) * kDW < 64, "vmcnt is six bits");
+  __host__ __device__ static constexpr int vswz(int key) {
+    return PKV_PREFILL_VSWZ == 1 ? (2 * key) % kRC
+         : PKV_PREFILL_VSWZ == 2 ? (4 * (key % 4) + (key / 4) % 4) % kRC
+                                 : key % kRC;
+  }
 };
 
 // Chunk rows per row tile: a tile holds 128 (head, row) pairs of one kv head.
@@ -289,11 +310,12 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   int local_bad = 0;
   // byte offset in a cache tile of the global chunk that lands at this lane's
   // LDS position in load i (row i * rows-per-load + lane / RC, swizzled chunk)
-  int goff[S::kLoadsPerWave];
+  int goff[S::kLoadsPerWave], goffv[S::kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < S::kLoadsPerWave; ++i) {
-    const int r = i * S::kRowsPerLoad + lane / RC;
+    const int r = i * S::kRowsPerLoad + lane / RC;  // the wave's 16 rows start at a multiple of 16
     goff[i] = r * RB + (((lane % RC) ^ (r % RC)) * 16);
+    goffv[i] = r * RB + (((lane % RC) ^ S::vswz(r)) * 16);
   }
   // Block of this wave in tile kt (uniform).  Blocks past the visible keys
   // read block 0 (their rows are never used: K rows past the keys are masked,
@@ -316,7 +338,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     for (int i = 0; i < S::kLoadsPerWave; ++i) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + goff[i]),
                                        (__attribute__((address_space(3))) void*)(kdst + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + goff[i]),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + goffv[i]),
                                        (__attribute__((address_space(3))) void*)(kdst + TB + i * 1024), 16, 0, 0);
     }
   };
@@ -342,7 +364,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int key = 8 * r + vkey, dim = 32 * nd + vdim;
-      voff[2 * nd + r] = TB + key * RB + (((dim >> 3) ^ (key % RC)) * 16) + (dim & 7) * 2;
+      voff[2 * nd + r] = key * RB + (((dim >> 3) ^ S::vswz(key)) * 16) + (dim & 7) * 2;
     }
 
   float m_run = kMaxInit, l_run = 0.0f;
@@ -353,67 +375,33 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     for (int v = 0; v < 16; ++v) oacc[nd][v] = 0.0f;
   const float sl2 = a.scale_log2;
 
-  // prologue: tiles 0 .. NS-2 in flight (past the last tile: zero rows, so every
-  // iteration finds the same number of loads outstanding)
-  int pnext = table_entry(kt0);
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t) {
-    const int p = pnext;
-    pnext = table_entry(kt0 + t + 1);
-    issue(kt0 + t, p);
-  }
-
   // a wave whose 32 rows carry no query only loads and synchronises
   const bool wave_active = __builtin_amdgcn_ballot_w64(row_ok) != 0;
 
-  // Tile kt: wait for its loads, start the loads of tile kt + NS - 1, then
-  // S^T = K Q^T, the online softmax and O^T += V^T P^T.  MASK: the tile holds
-  // keys past some row's position (diagonal tiles; the last one also holds
-  // keys past every row's, whose V rows are zeroed first).
-  auto tile = [&](auto mask_tag, int kt) {
+  // S^T = K Q^T for the tile whose K rows sit at LDS byte address kbase.
+  auto scores = [&](int kbase, f32x16_t (&st)[2]) {
+    int kb[S::kKSteps];
+#pragma unroll
+    for (int kk = 0; kk < S::kKSteps; ++kk) kb[kk] = kbase + koff[kk];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[nb][v] = 0.0f;
+      u32x4_t kv[S::kKSteps];
+      if (nb == 0) lds_read_b128<0>(kb, kv);
+      else lds_read_b128<32 * RB>(kb, kv);
+#pragma unroll
+      for (int kk = 0; kk < S::kKSteps; ++kk)
+        st[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[kk]), qop[kk], st[nb], 0, 0,
+                                                         0);
+    }
+  };
+
+  // The online softmax of tile kt's scores and O^T += V^T P^T with its V rows
+  // at LDS byte address vbase.  MASK: the tile holds keys past some row's
+  // position (diagonal tiles).
+  auto finish = [&](auto mask_tag, int kt, f32x16_t (&st)[2], int vbase) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    // this wave's loads of tile kt are done once at most NS-2 tiles' loads remain;
-    // the barrier then makes every wave's part visible and frees the stage of kt-1
-    wait_vmcnt_le<(NS - 2) * S::kDW>();
-    __builtin_amdgcn_s_barrier();
-    {
-      const int p = pnext;
-      pnext = table_entry(kt + NS);
-      issue(kt + NS - 1, p);
-    }
-    const int sbase = smem_base + (kt % NS) * S::kStageBytes;
-    if constexpr (MASK) {
-      const int r0 = kend - kt * kKT;  // rows [r0, 64) of the tile are past every row's keys
-      if (r0 < kKT) {
-        char* vt = smem + (kt % NS) * S::kStageBytes + TB;
-        for (int idx = tid; idx < (kKT - r0) * RC; idx += kThreads)
-          *reinterpret_cast<uint4*>(vt + (r0 + idx / RC) * RB + (idx % RC) * 16) = make_uint4(0u, 0u, 0u, 0u);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-      }
-    }
-    if (!wave_active) return;
-
-    f32x16_t st[2];
-    {
-      int kb[S::kKSteps];
-#pragma unroll
-      for (int kk = 0; kk < S::kKSteps; ++kk) kb[kk] = sbase + koff[kk];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st[nb][v] = 0.0f;
-        u32x4_t kv[S::kKSteps];
-        if (nb == 0) lds_read_b128<0>(kb, kv);
-        else lds_read_b128<32 * RB>(kb, kv);
-#pragma unroll
-        for (int kk = 0; kk < S::kKSteps; ++kk)
-          st[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[kk]), qop[kk], st[nb], 0,
-                                                           0, 0);
-      }
-    }
-
     // scale, causal mask (select, diagonal tiles only), row max over this lane and lane ^ 32
     float mx = -__builtin_inff();
 #pragma unroll
@@ -464,7 +452,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
         const bf16x8_t bop = as_bf16x8(pk[nb][4 * s], pk[nb][4 * s + 1], pk[nb][4 * s + 2], pk[nb][4 * s + 3]);
         int vb[NR];
 #pragma unroll
-        for (int i = 0; i < NR; ++i) vb[i] = sbase + voff[i];
+        for (int i = 0; i < NR; ++i) vb[i] = vbase + voff[i];
         u32x2_t vv[NR];
         if (nb == 0 && s == 0) lds_read_tr16<0>(vb, vv);
         else if (nb == 0) lds_read_tr16<16 * RB>(vb, vv);
@@ -476,8 +464,51 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
               as_bf16x8(vv[2 * nd].x, vv[2 * nd].y, vv[2 * nd + 1].x, vv[2 * nd + 1].y), bop, oacc[nd], 0, 0, 0);
       }
   };
+
+  // V rows [r0, 64) of the tile at LDS address vt are past every row's keys:
+  // zero them (they may hold NaN), visible to every wave before they are read.
+  auto zero_tail = [&](int kt, char* vt) {
+    const int r0 = kend - kt * kKT;
+    if (r0 < kKT) {
+      for (int idx = tid; idx < (kKT - r0) * RC; idx += kThreads)
+        *reinterpret_cast<uint4*>(vt + (r0 + idx / RC) * RB + (idx % RC) * 16) = make_uint4(0u, 0u, 0u, 0u);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
+  };
   // tiles with no key past any row's position, then the diagonal ones
   const int nfull = min(ntiles, mask_from / kKT);
+
+  // prologue: tiles 0 .. NS-2 in flight (past the last tile: zero rows, so every
+  // iteration finds the same number of loads outstanding)
+  int pnext = table_entry(kt0);
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) {
+    const int p = pnext;
+    pnext = table_entry(kt0 + t + 1);
+    issue(kt0 + t, p);
+  }
+  // Tile kt: wait for its loads, start the loads of tile kt + NS - 1, then
+  // S^T = K Q^T, the online softmax and O^T += V^T P^T (the last diagonal tile
+  // also holds keys past every row's, whose V rows are zeroed first).
+  auto tile = [&](auto mask_tag, int kt) {
+    // this wave's loads of tile kt are done once at most NS-2 tiles' loads remain;
+    // the barrier then makes every wave's part visible and frees the stage of kt-1
+    wait_vmcnt_le<(NS - 2) * S::kDW>();
+    __builtin_amdgcn_s_barrier();
+    {
+      const int p = pnext;
+      pnext = table_entry(kt + NS);
+      issue(kt + NS - 1, p);
+    }
+    const int sbase = smem_base + (kt % NS) * S::kStageBytes;
+    if constexpr (decltype(mask_tag)::value) zero_tail(kt, smem + (kt % NS) * S::kStageBytes + TB);
+    if (!wave_active) return;
+    f32x16_t st[2];
+    scores(sbase, st);
+    finish(mask_tag, kt, st, sbase + TB);
+  };
   for (int kt = kt0; kt < nfull; ++kt) tile(std::false_type{}, kt);
   for (int kt = max(kt0, nfull); kt < ntiles; ++kt) tile(std::true_type{}, kt);
 
