@@ -77,6 +77,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama3-8b-decode", choices=sorted(WORKLOADS))
+    p.add_argument("--streams", type=int, default=2, choices=[1, 2],
+                   help="mixed step: 2 runs the prefill chunks on a second stream beside the decode")
     p.add_argument("--partition", type=int, default=0,
                    help="decode partition tokens (0 = balanced split over a fixed number of wavefronts)")
     p.add_argument("--cold", action="store_true", help="overwrite 512 MB before every step (LLC-cold timing)")
@@ -188,8 +190,23 @@ def main():
         else:
             pkv.paged_attn_prefill_chunk_ws(qc, cstart, kc, vc, ctables, clens, scale, oc, workspace=pws)
 
+    # Mixed step on two streams: the prefill chunks do not depend on the decode,
+    # so after the cache write they run on a second stream (default priority)
+    # beside it -- the decode is bound by HBM, the chunks by the matrix cores.
+    two_streams = args.streams == 2 and w.num_seqs > 0 and has_chunks
+    side = torch.cuda.Stream() if two_streams else None
+    written = torch.cuda.Event() if two_streams else None
+
     def step():
         write()
+        if two_streams:
+            written.record()
+            side.wait_event(written)
+            decode()
+            with torch.cuda.stream(side):
+                prefill()
+            torch.cuda.current_stream().wait_stream(side)
+            return
         if w.num_seqs:
             decode()
         if has_chunks:
@@ -287,6 +304,7 @@ def main():
                             f"balanced over {pkv.decode_split_waves(w.num_q_heads, w.num_kv_heads)} wavefronts",
                    "kv_bytes_per_step": kv_bytes, "llc": "cold (512 MB overwrite per step)" if args.cold else "warm",
                    "kv_cache": "E4M3 codes + float32 scale per (slot, kv head)" if fp8 else w.dtype,
+                   "streams": 2 if two_streams else 1,
                    "layers_per_step": 1},
         "seq_tokens_per_s": round(seq_tok_s, 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

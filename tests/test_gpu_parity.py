@@ -371,6 +371,38 @@ def test_prefill_chunk_ws_parity(case):
         assert (got[c, n:] == SENTINEL).all()
 
 
+def test_mixed_step_on_two_streams():
+    """The mixed step with the prefill chunks on a second stream beside the decode
+    (after the cache write): both results still match the oracle."""
+    w = workloads.make(3)
+    dw = DeviceWorkload(w)
+    t = torch()
+    side = t.cuda.Stream()
+    written = t.cuda.Event()
+    pkv.paged_kv_write(dw.new_k, dw.new_v, dw.slots, dw.k_cache, dw.v_cache)
+    written.record()
+    side.wait_event(written)
+    out = empty_like_q(w.q.shape, w.dtype)
+    pkv.paged_attn_decode(dw.q, dw.k_cache, dw.v_cache, dw.tables, dw.lens, float(w.scale), out,
+                          max_context_len=w.max_context_len)
+    oc = empty_like_q(w.q_chunk.shape, w.dtype, fill_nan=False)
+    oc.fill_(SENTINEL)
+    with t.cuda.stream(side):
+        pkv.paged_attn_prefill_chunk_ws(dw.q_chunk, dw.chunk_start, dw.k_cache, dw.v_cache, dw.chunk_tables,
+                                        dw.chunk_lens, float(w.scale), oc)
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    rk, rv = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
+    check_attn(values(out), oracle.decode(w.q, rk, rv, w.block_tables, w.context_lens, w.scale, w.dtype), w.dtype,
+               "decode beside the chunks")
+    ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale,
+                               w.dtype)
+    got = values(oc)
+    for c in range(w.num_chunks):
+        n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+        check_attn(got[c, :n], ref[c, :n], w.dtype, f"chunk {c} beside the decode")
+
+
 def test_prefill_last_row_equals_decode():
     """The last row of a chunk is the decode query of the same position."""
     w = chunk_workload("bf16", 32, 8, 128, [(300, 200)], seed=12)
