@@ -216,6 +216,14 @@ int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const vo
   const size_t need = balanced ? balanced_workspace(num_q_heads, cache->num_kv_heads, cache->head_dim)
                                : partition_workspace(num_seqs, num_q_heads, cache->head_dim, max_context_len, part);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  // A batch whose every stream fits one wave's share of the balanced split
+  // (at most as many blocks in all as the split has waves) runs one wave per
+  // (sequence, head group) over its whole context: no partials, no merge
+  // kernel.  (The 4-sequence float32 batch: 15.5 us balanced.)
+  const int gb = heads_per_wave(num_q_heads / cache->num_kv_heads);
+  const int64_t streams = (int64_t)num_seqs * cache->num_kv_heads * ((num_q_heads / cache->num_kv_heads) / gb);
+  const bool whole = balanced && streams * (((int64_t)max_context_len + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE) <=
+                                     balanced_waves(gb);
   DecodeArgs a{};
   a.q = q;
   a.out = out;
@@ -238,7 +246,7 @@ int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const vo
   a.partition_tokens = part;
   a.max_parts = (int32_t)max_parts64;
   a.scale_log2 = scale * kLog2eHost;
-  a.balanced_waves = balanced ? balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads)) : 0;
+  a.balanced_waves = balanced && !whole ? balanced_waves(gb) : 0;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   return from_hip(launch_decode(a, as_stream(hip_stream)));

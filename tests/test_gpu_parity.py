@@ -379,14 +379,14 @@ def test_mixed_step_on_two_streams():
     t = torch()
     side = t.cuda.Stream()
     written = t.cuda.Event()
+    out = empty_like_q(w.q.shape, w.dtype)
+    oc = empty_like_q(w.q_chunk.shape, w.dtype, fill_nan=False)
+    oc.fill_(SENTINEL)  # before the event: the side stream must see it done
     pkv.paged_kv_write(dw.new_k, dw.new_v, dw.slots, dw.k_cache, dw.v_cache)
     written.record()
     side.wait_event(written)
-    out = empty_like_q(w.q.shape, w.dtype)
     pkv.paged_attn_decode(dw.q, dw.k_cache, dw.v_cache, dw.tables, dw.lens, float(w.scale), out,
                           max_context_len=w.max_context_len)
-    oc = empty_like_q(w.q_chunk.shape, w.dtype, fill_nan=False)
-    oc.fill_(SENTINEL)
     with t.cuda.stream(side):
         pkv.paged_attn_prefill_chunk_ws(dw.q_chunk, dw.chunk_start, dw.k_cache, dw.v_cache, dw.chunk_tables,
                                         dw.chunk_lens, float(w.scale), oc)
