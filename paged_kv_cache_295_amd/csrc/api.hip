@@ -111,7 +111,12 @@ ChunkSplit chunk_split(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads, 
   // unsplit against 78 us in pieces of 1024 keys plus a 14 us merge, while one
   // 512-row chunk at 3584 keys (128 units) takes 95 us unsplit, 58 + 18 us in
   // pieces of 512
-  if (2 * units >= kMatrixSlots || split >= max_keys) {
+  // Tiles whose rows fit one wave (the packed verify rows) write partials of
+  // at most 32 rows, so they split while units are fewer than the slots: 32
+  // sequences x 5 rows (256 units) 76 -> 63 us in four pieces; with a unit
+  // for every slot (64 sequences) any split was slower (115 -> 129..164 us).
+  const bool short_tile = rows_max * G <= 32;
+  if ((short_tile ? units >= kMatrixSlots : 2 * units >= kMatrixSlots) || split >= max_keys) {
     v.splits = 1;
     v.split_tokens = 0;
   } else {
