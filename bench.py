@@ -87,6 +87,8 @@ def parse():
     p.add_argument("--kv-dtype", choices=["model", "fp8"], default="model",
                    help="fp8: the cache held as E4M3 codes with per-(slot, kv head) scales (decode workloads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cold-check", action="store_true",
+                   help="skip the supplementary timing of the attention call with cold last-level caches")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     p.add_argument("--copy-pairs", type=int, default=512,
                    help="block pairs of the supplementary copy-on-write measurement (0: skip)")
@@ -253,6 +255,25 @@ def main():
         write_ms, dec_ms, pre_ms = write_ms - flush_ms, dec_ms - flush_ms, (pre_ms - flush_ms if has_chunks else 0.0)
         ms_per_step = max(ms_per_step - flush_ms, 1e-6)
 
+    # The same attention call with the last-level caches cold: a 512 MB
+    # overwrite (twice the MI355X's 256 MB Infinity Cache) before every call,
+    # its own time subtracted.  Warm repeated calls can find part of the batch's
+    # K/V still in that cache; this figure is the one bound by HBM alone.
+    cold_ms = None
+    main_call = decode if w.num_seqs else (prefill if verify else None)
+    if main_call is not None and flush is None and not args.no_cold_check:
+        buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+        def flushed():
+            buf.zero_()
+            main_call()
+        for _ in range(3):  # first touches of the new buffer are not part of either region
+            flushed()
+        n_cold = max(10, K // 4)
+        flush_only = timed(lambda: buf.zero_(), n_cold)
+        cold_ms = timed(flushed, n_cold) - flush_only
+        del buf
+
     eb = w.elem_bytes
     if verify:
         pb = accounting.prefill_bytes(w.chunk_start, w.chunk_context_lens, w.num_q_heads, w.num_kv_heads,
@@ -311,6 +332,11 @@ def main():
         "write_ms_mean": round(write_ms, 5),
         "decode_ms_mean": round(dec_ms, 5),
         "roofline": roofline,
+        "roofline_llc_cold": None if cold_ms is None else {
+            "launch_ms_mean": round(cold_ms, 5),
+            "achieved": round(dec["total"] / (cold_ms * 1e-3) / 1e9, 1),
+            "frac": round(dec["total"] / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "the same call after a 512 MB overwrite of the caches, the overwrite's time subtracted"},
     }
     if has_chunks:
         flops = accounting.prefill_flops(w.chunk_start, w.chunk_context_lens, w.num_q_heads, w.head_dim)

@@ -201,12 +201,15 @@ int paged_block_release(const int32_t* table, int32_t num_table_blocks, int32_t*
  *
  *   partition_tokens == 0 (recommended): balanced split.  The whole batch's
  *     work -- every (sequence, kv head, 16-token block) -- is divided over
- *     paged_attn_decode_split_waves(num_q_heads, num_kv_heads) wavefronts in
- *     runs of consecutive blocks.  Each (sequence, kv head) stream is charged
- *     its blocks plus a fixed cost for starting it, and every wavefront gets
- *     the same total charge, so all finish together whatever the mix of
+ *     paged_attn_decode_split_waves(num_q_heads, num_kv_heads) wavefronts (for
+ *     float32 / bf16 caches; fp8 caches use twice as many when that count is
+ *     1024) in runs of consecutive blocks.  Each (sequence, kv head) stream is
+ *     charged its blocks plus a fixed cost for starting it, and every wavefront
+ *     gets the same total charge, so all finish together whatever the mix of
  *     context lengths; a context is cut wherever a run ends.  The workspace
- *     size does not depend on the context lengths.
+ *     size does not depend on the context lengths or the cache dtype.  A batch
+ *     with no more blocks in all than wavefronts runs one wavefront per stream
+ *     over its whole context instead.
  *   partition_tokens > 0 (a multiple of 16): fixed partitions of that many
  *     tokens per sequence, one wavefront each.
  *

@@ -28,11 +28,11 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
-// Balanced split (partition_tokens == 0): balanced_waves(gb) waves, each with
+// Balanced split (partition_tokens == 0): up to balanced_waves_max(gb) waves, each with
 // up to two partials of gb = heads_per_wave heads.
 size_t balanced_workspace(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
   const int gb = heads_per_wave(num_q_heads / num_kv_heads);
-  return (size_t)balanced_waves(gb) * 2 * gb * ((size_t)head_dim + 2) * sizeof(float);
+  return (size_t)balanced_waves_max(gb) * 2 * gb * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 // Fixed partitions of `part` tokens: one partial per (row, head, partition).
@@ -180,7 +180,7 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* cac
 
 int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
-  return balanced_waves(heads_per_wave(num_q_heads / num_kv_heads));
+  return balanced_waves(heads_per_wave(num_q_heads / num_kv_heads), PKV_DTYPE_BF16);
 }
 
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -228,7 +228,7 @@ int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const vo
   const int gb = heads_per_wave(num_q_heads / cache->num_kv_heads);
   const int64_t streams = (int64_t)num_seqs * cache->num_kv_heads * ((num_q_heads / cache->num_kv_heads) / gb);
   const bool whole = balanced && streams * (((int64_t)max_context_len + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE) <=
-                                     balanced_waves(gb);
+                                     balanced_waves(gb, cache->dtype);
   DecodeArgs a{};
   a.q = q;
   a.out = out;
@@ -251,7 +251,8 @@ int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const vo
   a.partition_tokens = part;
   a.max_parts = (int32_t)max_parts64;
   a.scale_log2 = scale * kLog2eHost;
-  a.balanced_waves = balanced && !whole ? balanced_waves(gb) : 0;
+  a.balanced_waves = balanced && !whole ? balanced_waves(gb, cache->dtype) : 0;
+  a.max_context_tokens = max_context_len;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   return from_hip(launch_decode(a, as_stream(hip_stream)));
@@ -398,7 +399,7 @@ int paged_attn_decode_shared_prefix(const void* q, int32_t num_seqs, int32_t num
   a.partition_tokens = max_blocks_per_seq * PKV_BLOCK_SIZE;
   a.max_parts = 1;
   a.scale_log2 = sl2;
-  a.balanced_waves = balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads));
+  a.balanced_waves = balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads), cache->dtype);
   if (prefix_len > 0) {
     a.init_o = pre_o;
     a.init_ml = pre_o + (size_t)ps.splits * num_seqs * num_q_heads * cache->head_dim;

@@ -34,6 +34,8 @@
 //    otherwise each partition writes (m, l, unnormalised o) and the merge
 //    kernel combines them: M = max m_p, out = sum 2^(m_p - M) o_p / sum
 //    2^(m_p - M) l_p, exact in real arithmetic.
+#include <type_traits>
+
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 
@@ -978,8 +980,9 @@ hipError_t launch_prefix_merge(float* part_o, float* part_ml, int64_t rows, int 
 #ifndef PKV_DECODE_LPT_SMALL_GROUP
 #define PKV_DECODE_LPT_SMALL_GROUP 8
 #endif
+// Register stages of the K/V pipeline (0: by type, see pipeline_stages).
 #ifndef PKV_DECODE_STAGES
-#define PKV_DECODE_STAGES 2
+#define PKV_DECODE_STAGES 0
 #endif
 // fp8 at head_dim 128 keeps 8 lanes per token: 4 (two blocks per pipeline
 // tile, half the replicated softmax work) was measured slower, 72.8 us against
@@ -994,17 +997,24 @@ constexpr int lanes_per_token() {
   constexpr int want = GB >= 8 ? 16 : (KvTraits<KV>::kScaled ? PKV_DECODE_LPT_FP8 : PKV_DECODE_LPT_SMALL_GROUP);
   return row_chunks < want ? row_chunks : want;
 }
-// Register stages of the K/V prefetch pipeline (fixed partitions).
+// Register stages of the K/V prefetch pipeline.  bf16 with up to four heads
+// per wave runs at one wave per SIMD; for long contexts it keeps four blocks in
+// flight (cold caches, the Llama-3-8B batch: 95-98 us against 102 us with two),
+// while short ones keep two, whose pipeline fills faster at every segment start
+// (the shared-prefix suffixes of at most 512 tokens: 101 us against 110 us).
+// The types and groups that run two waves per SIMD, or need the registers
+// (float32), keep two.
 template <typename KV, int D, int GB>
-constexpr int pipeline_stages() {
-  return PKV_DECODE_STAGES;
+constexpr int deep_stages() {
+  if (PKV_DECODE_STAGES > 0) return PKV_DECODE_STAGES;
+  return (std::is_same<KV, __bf16>::value && GB <= 4) ? 4 : 2;
 }
+constexpr int kDeepPipelineMinTokens = 1024;  // longest context from which the deep pipeline pays
 
-template <typename KV, int D, int GB>
-static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+template <typename KV, int D, int GB, int NS>
+static hipError_t launch_stages(const DecodeArgs& a, hipStream_t stream) {
   using T = typename KvTraits<KV>::Q;
   constexpr int LPT = lanes_per_token<KV, D, GB>();
-  constexpr int NS = pipeline_stages<KV, D, GB>();
   if (a.balanced_waves > 0) {
     const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
     const int64_t merges = (int64_t)a.num_seqs * a.num_kv_heads * hsubs;
@@ -1030,6 +1040,15 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)merges), dim3(64), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename KV, int D, int GB>
+static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int NSD = deep_stages<KV, D, GB>();
+  if constexpr (NSD != 2) {
+    if (a.max_context_tokens >= kDeepPipelineMinTokens) return launch_stages<KV, D, GB, NSD>(a, stream);
+  }
+  return launch_stages<KV, D, GB, 2>(a, stream);
 }
 
 template <typename KV, int D>

@@ -321,6 +321,22 @@ def test_spec_verify_parity(case):
         assert (got[c, n:] == SENTINEL).all(), "rows past the sequence's count must not be written"
 
 
+@pytest.mark.parametrize("name", ["spec-verify", "spec-verify-b8"])
+def test_spec_verify_bench_workloads(name):
+    """The benchmark's verify batches (64 and 8 sequences x 5 rows, contexts U{128..4096}) through the call
+    and the launch configuration the benchmark times."""
+    w = workloads.make(name)
+    dw = DeviceWorkload(w)
+    rk, rv = run_write(dw)
+    out, need = run_verify(dw)
+    say(f"{w.name}: workspace {need} bytes")
+    ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale,
+                               w.dtype)
+    got = values(out)
+    n = w.q_chunk.shape[1]
+    check_attn(got[:, :n], ref[:, :n], w.dtype, name)
+
+
 def test_spec_verify_split_bad_sequence_gives_nan():
     """A sequence that breaks the contract (more rows than rows_max) gets NaN rows;
     the others are unaffected, with the keys split into pieces."""
