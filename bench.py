@@ -41,10 +41,10 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 # only for the decode kernel sources it was measured on: reported as null once
 # their hash differs.
 TRAFFIC = {
-    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 520795955, "write_bytes": 3421696,
-                                        "sources_sha256": "98e5972c1a701758288e3b30885f3b2a40229fd9cc9eb1c1459cf41424e0b741"},
-    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 278239027, "write_bytes": 3419750,
-                                      "sources_sha256": "98e5972c1a701758288e3b30885f3b2a40229fd9cc9eb1c1459cf41424e0b741"},
+    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 529853030, "write_bytes": 3422208,
+                                        "sources_sha256": "d32406bd3a7007fd24d92d202b414f073d8c6acc61485ddeea01b19e97d9316e"},
+    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 284376064, "write_bytes": 5462528,
+                                      "sources_sha256": "d32406bd3a7007fd24d92d202b414f073d8c6acc61485ddeea01b19e97d9316e"},
 }
 CSRC = os.path.join(ROOT, "paged_kv_cache_295_amd", "csrc")
 DECODE_SOURCES = ("decode.hip", "pkv_device.hpp", "pkv_internal.hpp")
