@@ -754,32 +754,55 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
   const int HH = a.num_kv_heads * hsubs;  // streams per sequence
   const int cap = a.max_blocks_per_seq * kBlock;
 
-  int64_t U, unused;
-  cost_counts(lens, B, 0, cap, HH, U, unused);
-  const int64_t u0 = range_begin(w, W, U), u1 = range_begin(w + 1, W, U);
-  if (u0 >= u1) return;
-
-  // locate u0: the sequence s whose cost interval [cum, cum + cost) holds it
+  // A batch of at most 64 sequences keeps every length in a lane: one load
+  // gives the total cost, this wave's first sequence and every later length
+  // (the start of the kernel is one dependent load shorter, and moving to the
+  // next sequence needs none).
+  const bool small = B <= kWave;
+  const int Llane = small && lane < B ? lens[lane] : 0;
+  int64_t U;
   int s = 0;
   int64_t cum = 0;
-  for (int c0 = 0; c0 < B; c0 += kWave) {
-    const int i = c0 + lane;
-    const int64_t c = i < B ? seq_cost(seq_blocks(lens[i], cap), HH) : 0;
+  int L;
+  int64_t u0, u1;
+  if (small) {
+    const int64_t c = lane < B ? seq_cost(seq_blocks(Llane, cap), HH) : 0;
     const int64_t incl = wave_incl_scan(c);
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && cum + incl > u0);
-    if (hit) {
-      const int ln = __builtin_ctzll(hit);
-      s = c0 + ln;
-      cum += readlane64(incl - c, ln);
-      break;
+    U = uniform64(readlane64(incl, kWave - 1));
+    u0 = range_begin(w, W, U);
+    u1 = range_begin(w + 1, W, U);
+    if (u0 >= u1) return;
+    // the sequence s whose cost interval [cum, cum + cost) holds u0 (one exists: u0 < U)
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && incl > u0);
+    s = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+    cum = uniform64(readlane64(incl - c, s));
+    L = __builtin_amdgcn_readlane(Llane, s);
+  } else {
+    int64_t unused;
+    cost_counts(lens, B, 0, cap, HH, U, unused);
+    u0 = range_begin(w, W, U);
+    u1 = range_begin(w + 1, W, U);
+    if (u0 >= u1) return;
+    // locate u0: the sequence s whose cost interval [cum, cum + cost) holds it
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const int i = c0 + lane;
+      const int64_t c = i < B ? seq_cost(seq_blocks(lens[i], cap), HH) : 0;
+      const int64_t incl = wave_incl_scan(c);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && cum + incl > u0);
+      if (hit) {
+        const int ln = __builtin_ctzll(hit);
+        s = c0 + ln;
+        cum += readlane64(incl - c, ln);
+        break;
+      }
+      cum += readlane64(incl, kWave - 1);
     }
-    cum += readlane64(incl, kWave - 1);
+    s = __builtin_amdgcn_readfirstlane(s);
+    cum = uniform64(cum);
+    L = lens[s];
   }
-  s = __builtin_amdgcn_readfirstlane(s);
-  cum = uniform64(cum);
 
   Segment<KV, D, GB, LPT, NS> seg(a);
-  int L = lens[s];
   int nb = seq_blocks(L, cap);
   bool first = true;
   for (int64_t u = u0;;) {
@@ -809,7 +832,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
       cum += (int64_t)HH * span;
       do {
         ++s;
-        L = lens[s];
+        L = small ? __builtin_amdgcn_readlane(Llane, s) : lens[s];
         nb = seq_blocks(L, cap);
       } while (nb == 0);
     }
@@ -901,6 +924,22 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
       mc[h] = owner ? a.part_ml[(slot * GB + h) * 2] : -__builtin_inff();
       lc[h] = owner ? a.part_ml[(slot * GB + h) * 2 + 1] : 0.0f;
     }
+    // the outputs of the first kPre candidates do not depend on the (m, l)
+    // values: their loads go out together with them (a stream has two or three
+    // owners at most unless it is much longer than a wave's range)
+    constexpr int kPre = 4;
+    const uint64_t owners = __builtin_amdgcn_ballot_w64(owner);
+    float opre[kPre][GB][PER];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const bool oj = (owners >> j) & 1ull;
+      // slot 0 for a non-owner: the address stays inside the workspace even if the load is issued
+      const int64_t sj = oj ? __builtin_amdgcn_readlane((int)(slot & 0x7fffffff), j) : 0;
+#pragma unroll
+      for (int h = 0; h < GB; ++h)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) opre[j][h][e] = oj ? a.part_o[(sj * GB + h) * D + lane + e * kWave] : 0.0f;
+    }
     float f[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
@@ -913,10 +952,19 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
       M[h] = Mn;
     }
     // pass 2: weighted sum of the owners' outputs (loads of four owners in flight)
-    const uint64_t owners = __builtin_amdgcn_ballot_w64(owner);
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      if (!((owners >> j) & 1ull)) continue;
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f[h]), j));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[h][e] = fmaf(fj, opre[j][h][e], o[h][e]);
+      }
+    }
     const int n = 64 - __builtin_clzll(owners | 1ull);
 #pragma unroll 4
-    for (int j = 0; j < n; ++j) {
+    for (int j = kPre; j < n; ++j) {
       if (!((owners >> j) & 1ull)) continue;
       const int64_t sj = __builtin_amdgcn_readlane((int)(slot & 0x7fffffff), j);
 #pragma unroll
