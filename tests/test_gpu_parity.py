@@ -419,6 +419,56 @@ def test_mixed_step_on_two_streams():
         check_attn(got[c, :n], ref[c, :n], w.dtype, f"chunk {c} beside the decode")
 
 
+def test_mixed_step_in_a_hip_graph():
+    """The library allocates nothing, clears nothing with memset and keeps no
+    state between calls, so a step (cache write, decode with the merge of cut
+    streams, prefill chunks) can be captured in a HIP graph.  Every replay, with
+    eager work and synchronisations between replays, gives the eager result bit
+    for bit, and the eager result matches the oracle."""
+    w = workloads.make(3)
+    dw = DeviceWorkload(w)
+    t = torch()
+    out = empty_like_q(w.q.shape, w.dtype)
+    oc = empty_like_q(w.q_chunk.shape, w.dtype, fill_nan=False)
+    ws = t.empty(pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                            w.max_context_len, 0), dtype=t.uint8, device=device())
+    pws = t.empty(max(1, pkv.prefill_chunk_workspace_bytes(w.num_chunks, w.q_chunk.shape[1], w.num_q_heads,
+                                                           w.num_kv_heads, w.head_dim, w.chunk_tables.shape[1])),
+                  dtype=t.uint8, device=device())
+
+    def step():
+        pkv.paged_kv_write(dw.new_k, dw.new_v, dw.slots, dw.k_cache, dw.v_cache)
+        pkv.paged_attn_decode(dw.q, dw.k_cache, dw.v_cache, dw.tables, dw.lens, float(w.scale), out,
+                              max_context_len=w.max_context_len, workspace=ws)
+        pkv.paged_attn_prefill_chunk_ws(dw.q_chunk, dw.chunk_start, dw.k_cache, dw.v_cache, dw.chunk_tables,
+                                        dw.chunk_lens, float(w.scale), oc, workspace=pws)
+
+    oc.fill_(SENTINEL)
+    step()
+    t.cuda.synchronize()
+    eager_out, eager_oc = bits(out), bits(oc)
+    rk, rv = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
+    check_attn(values(out), oracle.decode(w.q, rk, rv, w.block_tables, w.context_lens, w.scale, w.dtype), w.dtype,
+               "eager decode")
+
+    g = t.cuda.CUDAGraph()
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        with t.cuda.graph(g, stream=side):
+            step()
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))  # eager work between the replays
+        oc.fill_(SENTINEL)
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(bits(out), eager_out), f"graph replay {rep}: decode differs from the eager call"
+        assert np.array_equal(bits(oc), eager_oc), f"graph replay {rep}: chunks differ from the eager call"
+
+
 def test_prefill_last_row_equals_decode():
     """The last row of a chunk is the decode query of the same position."""
     w = chunk_workload("bf16", 32, 8, 128, [(300, 200)], seed=12)
