@@ -839,37 +839,47 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
   }
 }
 
-// One wave per (sequence, stream): writes NaN / 0 for sequences with an
-// invalid / empty context, and merges the partials of a stream that was cut
-// across wave ranges.  The loads are issued together, not one owner after the
-// other: lane j examines candidate wave wf + j (the owners of a stream are
-// consecutive waves, except for empty ranges when waves outnumber units) and
-// loads its (m, l) for every head; the outputs then sum over the owners with
-// lane k owning dims k, k + 64, ...
-template <typename T, int D, int GB>
+// One wave per (sequence, stream, HM heads of the stream's group of GB):
+// writes NaN / 0 for sequences with an invalid / empty context, and merges the
+// partials of a stream that was cut across wave ranges.  The loads are issued
+// together, not one owner after the other: lane j examines candidate wave
+// wf + j (the owners of a stream are consecutive waves, except for empty
+// ranges when waves outnumber units) and loads its (m, l); the outputs of the
+// first kPre owners are loaded at the same time, and the sum over the owners
+// has lane k owning dims k, k + 64, ...  HM = 1 (one head per wave) suits
+// batches of few, long streams: the long-context batch's 64 streams have 32
+// owners each, and its merge takes 14 us against 21 us with the whole group
+// per wave; with many streams every wave repeats the cost scan over the
+// lengths, and the whole group per wave is faster (the 256-sequence batch:
+// 2048 streams, 6.0 us against 10 us).
+template <typename T, int D, int GB, int HM>
 __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeArgs a, int W) {
   constexpr int PER = D / kWave;
+  constexpr int kPre = HM == 1 ? 16 : 4;
+  static_assert(GB % HM == 0, "a wave takes a whole share of the group");
   const int lane = __lane_id();
   const int B = a.num_seqs;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int hsubs = G / GB;
   const int HH = a.num_kv_heads * hsubs;
   const int cap = a.max_blocks_per_seq * kBlock;
-  const int s = blockIdx.x / HH;
-  const int k = blockIdx.x - s * HH;
+  const int hh0 = (blockIdx.x % (GB / HM)) * HM;  // first head of this wave within the stream's group
+  const int stream = blockIdx.x / (GB / HM);       // (sequence, stream)
+  const int s = stream / HH;
+  const int k = stream - s * HH;
   const int g = k / hsubs, hs = k - g * hsubs;
-  const int h0 = g * G + hs * GB;
-  T* outp = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D;
+  const int head0 = g * G + hs * GB + hh0;
+  T* outp = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + head0) * D;
 
   const int L = a.context_lens[s];
   if (L == 0 && a.init_o != nullptr) {  // nothing after the shared prefix: its state alone
     const int64_t split_stride = (int64_t)B * a.num_q_heads;
-    const int64_t row = (int64_t)s * a.num_q_heads + h0;
-    for (int h = 0; h < GB; ++h) {
+    const int64_t row0 = (int64_t)s * a.num_q_heads + head0;
+    for (int h = 0; h < HM; ++h) {
       float M = -__builtin_inff();
       bool nan = false;
       for (int sp = 0; sp < a.init_splits; ++sp) {
-        const float ms = a.init_ml[(sp * split_stride + row + h) * 2];
+        const float ms = a.init_ml[(sp * split_stride + row0 + h) * 2];
         nan |= ms != ms;
         M = fmaxf(M, ms);
       }
@@ -877,7 +887,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
 #pragma unroll
       for (int e = 0; e < PER; ++e) o[e] = 0.0f;
       for (int sp = 0; sp < a.init_splits; ++sp) {
-        const int64_t r = sp * split_stride + row + h;
+        const int64_t r = sp * split_stride + row0 + h;
         const float f = fast_exp2(a.init_ml[r * 2] - M);
         lam = fmaf(f, a.init_ml[r * 2 + 1], lam);
 #pragma unroll
@@ -891,7 +901,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
   }
   if (L < 0 || L > cap || L == 0) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
-    for (int i = lane; i < GB * D; i += kWave) outp[i] = (T)fill;
+    for (int i = lane; i < HM * D; i += kWave) outp[i] = (T)fill;
     return;
   }
   int64_t U, before;
@@ -903,9 +913,9 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
   const int wf = wave_of(us, W, U), wl = wave_of(ue, W, U);
   if (wf == wl) return;  // finished inside one wave
 
-  float M[GB], lam[GB], o[GB][PER];
+  float M[HM], lam[HM], o[HM][PER];
 #pragma unroll
-  for (int h = 0; h < GB; ++h) {
+  for (int h = 0; h < HM; ++h) {
     M[h] = -__builtin_inff();
     lam[h] = 0.0f;
 #pragma unroll
@@ -918,31 +928,30 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
     const bool owner = c <= wl && rb < range_begin(c + 1, W, U);  // non-empty range inside [wf, wl]
     // slot 1 if wave c worked on an earlier stream first, i.e. its range starts before this stream's
     const int64_t slot = (int64_t)c * 2 + ((c == wf && rb < as) ? 1 : 0);
-    float mc[GB], lc[GB];
+    float mc[HM], lc[HM];
 #pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      mc[h] = owner ? a.part_ml[(slot * GB + h) * 2] : -__builtin_inff();
-      lc[h] = owner ? a.part_ml[(slot * GB + h) * 2 + 1] : 0.0f;
+    for (int h = 0; h < HM; ++h) {
+      mc[h] = owner ? a.part_ml[(slot * GB + hh0 + h) * 2] : -__builtin_inff();
+      lc[h] = owner ? a.part_ml[(slot * GB + hh0 + h) * 2 + 1] : 0.0f;
     }
     // the outputs of the first kPre candidates do not depend on the (m, l)
-    // values: their loads go out together with them (a stream has two or three
-    // owners at most unless it is much longer than a wave's range)
-    constexpr int kPre = 4;
+    // values: their loads go out together with them
     const uint64_t owners = __builtin_amdgcn_ballot_w64(owner);
-    float opre[kPre][GB][PER];
+    float opre[kPre][HM][PER];
 #pragma unroll
     for (int j = 0; j < kPre; ++j) {
       const bool oj = (owners >> j) & 1ull;
       // slot 0 for a non-owner: the address stays inside the workspace even if the load is issued
       const int64_t sj = oj ? __builtin_amdgcn_readlane((int)(slot & 0x7fffffff), j) : 0;
 #pragma unroll
-      for (int h = 0; h < GB; ++h)
+      for (int h = 0; h < HM; ++h)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) opre[j][h][e] = oj ? a.part_o[(sj * GB + h) * D + lane + e * kWave] : 0.0f;
+        for (int e = 0; e < PER; ++e)
+          opre[j][h][e] = oj ? a.part_o[(sj * GB + hh0 + h) * D + lane + e * kWave] : 0.0f;
     }
-    float f[GB];
+    float f[HM];
 #pragma unroll
-    for (int h = 0; h < GB; ++h) {
+    for (int h = 0; h < HM; ++h) {
       const float Mn = fmaxf(M[h], wave_max(mc[h]));
       const float rescale = fast_exp2(M[h] - Mn);  // earlier chunks of owners
       f[h] = owner ? fast_exp2(mc[h] - Mn) : 0.0f;
@@ -951,12 +960,12 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
       for (int e = 0; e < PER; ++e) o[h][e] *= rescale;
       M[h] = Mn;
     }
-    // pass 2: weighted sum of the owners' outputs (loads of four owners in flight)
+    // pass 2: weighted sum of the owners' outputs
 #pragma unroll
     for (int j = 0; j < kPre; ++j) {
       if (!((owners >> j) & 1ull)) continue;
 #pragma unroll
-      for (int h = 0; h < GB; ++h) {
+      for (int h = 0; h < HM; ++h) {
         const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f[h]), j));
 #pragma unroll
         for (int e = 0; e < PER; ++e) o[h][e] = fmaf(fj, opre[j][h][e], o[h][e]);
@@ -968,15 +977,16 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
       if (!((owners >> j) & 1ull)) continue;
       const int64_t sj = __builtin_amdgcn_readlane((int)(slot & 0x7fffffff), j);
 #pragma unroll
-      for (int h = 0; h < GB; ++h) {
+      for (int h = 0; h < HM; ++h) {
         const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f[h]), j));
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[h][e] = fmaf(fj, a.part_o[(sj * GB + h) * D + lane + e * kWave], o[h][e]);
+        for (int e = 0; e < PER; ++e)
+          o[h][e] = fmaf(fj, a.part_o[(sj * GB + hh0 + h) * D + lane + e * kWave], o[h][e]);
       }
     }
   }
 #pragma unroll
-  for (int h = 0; h < GB; ++h) {
+  for (int h = 0; h < HM; ++h) {
     const float inv = 1.0f / lam[h];
 #pragma unroll
     for (int e = 0; e < PER; ++e) outp[h * D + lane + e * kWave] = (T)(o[h][e] * inv);
@@ -1059,20 +1069,28 @@ constexpr int deep_stages() {
 }
 constexpr int kDeepPipelineMinTokens = 1024;  // longest context from which the deep pipeline pays
 
+// Merge grids of at most this many waves take one head per wave.
+constexpr int64_t kMergeWavesPerHead = 4096;
+
 template <typename KV, int D, int GB, int NS>
 static hipError_t launch_stages(const DecodeArgs& a, hipStream_t stream) {
   using T = typename KvTraits<KV>::Q;
   constexpr int LPT = lanes_per_token<KV, D, GB>();
   if (a.balanced_waves > 0) {
     const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
-    const int64_t merges = (int64_t)a.num_seqs * a.num_kv_heads * hsubs;
-    if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int64_t streams = (int64_t)a.num_seqs * a.num_kv_heads * hsubs;
+    if (streams * GB > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_balanced_kernel<KV, D, GB, LPT, NS>), dim3(a.balanced_waves), dim3(64), 0, stream, a,
                        a.block_tables, a.context_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_balanced_merge_kernel<T, D, GB>), dim3((unsigned)merges), dim3(64), 0, stream, a,
-                       a.balanced_waves);
+    // one head per merge wave while that keeps the grid small (few, long streams)
+    if (streams * GB <= kMergeWavesPerHead)
+      hipLaunchKernelGGL((decode_balanced_merge_kernel<T, D, GB, 1>), dim3((unsigned)(streams * GB)), dim3(64), 0,
+                         stream, a, a.balanced_waves);
+    else
+      hipLaunchKernelGGL((decode_balanced_merge_kernel<T, D, GB, GB>), dim3((unsigned)streams), dim3(64), 0, stream,
+                         a, a.balanced_waves);
     return hipGetLastError();
   }
   const int64_t rows = (int64_t)a.num_seqs * a.rows_per_seq;
