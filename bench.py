@@ -68,6 +68,7 @@ WORKLOADS = {
     "long-context": 5,
     "spec-verify": "spec-verify",  # supplementary: speculative-decoding verify (5-row chunks)
     "spec-verify-b8": "spec-verify-b8",  # the same with 8 sequences (keys split over the GPU)
+    "prefill-large": "prefill-large",  # supplementary: 16 chunks x 512 rows at 3584 keys (matrix-core bound)
 }
 
 
@@ -174,7 +175,8 @@ def main():
             pkv.paged_attn_decode(q, kc, vc, tables, lens, scale, out, max_context_len=w.max_context_len,
                                   partition_tokens=part, workspace=ws)
 
-    verify = w.num_seqs == 0 and has_chunks  # the speculative-verify pass: chunk rows only
+    verify = w.num_seqs == 0 and has_chunks  # chunk rows only: the verify pass, or the large prefill
+    prefill_only = cfg == "prefill-large"
     if verify:
         vws = torch.empty(max(1, pkv.spec_verify_workspace_bytes(w.num_chunks, w.q_chunk.shape[1], w.num_q_heads,
                                                                 w.num_kv_heads, w.head_dim, w.chunk_tables.shape[1])),
@@ -187,8 +189,10 @@ def main():
                           dtype=torch.uint8, device=dev)
 
     def prefill():
-        if verify:
+        if verify and not prefill_only:
             pkv.paged_attn_spec_verify(qc, cstart, kc, vc, ctables, clens, scale, oc, workspace=vws)
+        elif prefill_only:
+            pkv.paged_attn_prefill_chunk_ws(qc, cstart, kc, vc, ctables, clens, scale, oc, workspace=vws)
         else:
             pkv.paged_attn_prefill_chunk_ws(qc, cstart, kc, vc, ctables, clens, scale, oc, workspace=pws)
 
@@ -294,18 +298,26 @@ def main():
     traffic = None
     if tr is not None and tr["sources_sha256"] == sources_sha256() and part == 0 and not args.cold and not verify:
         traffic = tr["read_bytes"] + tr["write_bytes"]
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "paged_attn_spec_verify: prefill_mfma_kernel<split> + prefill_split_merge_kernel"
-                if verify else
-                          ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
-                           "decode_balanced_kernel + decode_balanced_merge_kernel") if cascade else
-                          ("paged_attn_decode_fp8: decode_balanced_kernel<fp8> + decode_balanced_merge_kernel"
-                           if fp8 and part == 0 else
-                           "paged_attn_decode: decode_balanced_kernel + decode_balanced_merge_kernel"
-                           if part == 0 else "paged_attn_decode: decode_partition_kernel + decode_merge_kernel"),
-                "algorithmic_bytes_per_launch": dec["total"], "launch_ms_mean": round(launch_ms, 5),
-                "traffic_read_write_bytes": [tr["read_bytes"], tr["write_bytes"]] if traffic else None}
+    if prefill_only:  # matrix-core bound: causal-pair FLOPs of the call against the dense bf16 peak
+        fl = accounting.prefill_flops(w.chunk_start, w.chunk_context_lens, w.num_q_heads, w.head_dim)
+        tf = fl / (launch_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "paged_attn_prefill_chunk_ws: prefill_mfma_kernel<chunk>",
+                    "algorithmic_flops_per_launch": fl, "launch_ms_mean": round(launch_ms, 5)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "paged_attn_spec_verify: prefill_mfma_kernel<split> + prefill_split_merge_kernel"
+                    if verify else
+                              ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
+                               "decode_balanced_kernel + decode_balanced_merge_kernel") if cascade else
+                              ("paged_attn_decode_fp8: decode_balanced_kernel<fp8> + decode_balanced_merge_kernel"
+                               if fp8 and part == 0 else
+                               "paged_attn_decode: decode_balanced_kernel + decode_balanced_merge_kernel"
+                               if part == 0 else "paged_attn_decode: decode_partition_kernel + decode_merge_kernel"),
+                    "algorithmic_bytes_per_launch": dec["total"], "launch_ms_mean": round(launch_ms, 5),
+                    "traffic_read_write_bytes": [tr["read_bytes"], tr["write_bytes"]] if traffic else None}
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -317,7 +329,8 @@ def main():
                    "block_size": 16, "num_blocks": w.num_blocks,
                    "context_tokens": int((w.chunk_context_lens if verify else w.context_lens).sum()),
                    "max_context_len": w.max_context_len,
-                   "split": ("keys of each (sequence, kv head) cut into pieces" if w.num_chunks * w.num_kv_heads < 256
+                   "split": "one workgroup per (chunk, kv head, 128-row tile)" if prefill_only else
+                            ("keys of each (sequence, kv head) cut into pieces" if w.num_chunks * w.num_kv_heads < 256
                              else "one workgroup per (sequence, kv head)") if verify else
                             f"fixed partitions of {part} tokens" if part else
                             (f"shared prefix of {len(w.shared_blocks) * 16} tokens attended once, then " if cascade
@@ -334,8 +347,10 @@ def main():
         "roofline": roofline,
         "roofline_llc_cold": None if cold_ms is None else {
             "launch_ms_mean": round(cold_ms, 5),
-            "achieved": round(dec["total"] / (cold_ms * 1e-3) / 1e9, 1),
-            "frac": round(dec["total"] / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "achieved": round(roofline["algorithmic_flops_per_launch"] / (cold_ms * 1e-3) / 1e12, 1) if prefill_only
+            else round(dec["total"] / (cold_ms * 1e-3) / 1e9, 1),
+            "frac": round(roofline["algorithmic_flops_per_launch"] / (cold_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            if prefill_only else round(dec["total"] / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "the same call after a 512 MB overwrite of the caches, the overwrite's time subtracted"},
     }
     if has_chunks:
@@ -366,7 +381,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
-    if not args.no_cpu_baseline and not fp8:
+    if not args.no_cpu_baseline and not fp8 and not prefill_only:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, cfg)
     print(json.dumps(res), flush=True)
 

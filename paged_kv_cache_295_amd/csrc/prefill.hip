@@ -243,8 +243,17 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
       sp = t % a.num_splits;
       t /= a.num_splits;
     }
-    const int pair = t % npair;
-    const int mt = n_mt - 1 - t / npair;  // the longest row tiles start first
+    int pair = t % npair;
+    int mt = n_mt - 1 - t / npair;  // the longest row tiles start first
+    if (MODE == kChunk && npair % 8 == 0) {
+      // Workgroups go to the eight XCDs round-robin by id.  Give each XCD its
+      // pairs (pair mod 8) one after the other, all row tiles of a pair at
+      // consecutive slots (longest first): they read the same key tiles at
+      // about the same time, from that XCD's L2.
+      const int x = t % 8, j = t / 8;
+      pair = x + 8 * (j / n_mt);
+      mt = n_mt - 1 - j % n_mt;
+    }
     c = pair / a.num_kv_heads;
     g = pair - c * a.num_kv_heads;
 

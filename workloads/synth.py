@@ -385,6 +385,18 @@ def spec_verify(seed: Optional[int] = None, batch: int = 64, k: int = 4, lo: int
                              "32q/8kv x 128, bf16")
 
 
+def prefill_large(seed: Optional[int] = None, chunks: int = 16, rows: int = 512, start: int = 3584) -> Workload:
+    """Large chunked prefill: 16 chunks of 512 rows at position 3584 of 4096-token prompts,
+    32 q / 8 kv heads x 128, bf16.  Not one of the five serving mixes: a prefill big
+    enough that the matrix cores, not the launch, set its time."""
+    seed = SEED_BASE + 7 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seqs = [SeqSpec(start + rows, n_new=rows, kind="chunk") for _ in range(chunks)]
+    return build("prefill-large-bf16", seed, "bf16", 32, 8, 128, seqs,
+                 max_blocks_chunk=-(-(start + rows) // BLOCK_SIZE), chunk_len_max=rows, rng=rng,
+                 description=f"{chunks} chunks x {rows} rows at position {start}, 32q/8kv x 128, bf16")
+
+
 CONFIGS = {
     1: tiny_f32,
     2: llama8b_decode,
@@ -398,6 +410,7 @@ CONFIGS = {
 SUPPLEMENTARY = {
     "spec-verify": spec_verify,
     "spec-verify-b8": lambda seed=None: spec_verify(seed, batch=8),
+    "prefill-large": prefill_large,
 }
 
 
