@@ -99,6 +99,34 @@ def test_config_parity(cfg):
         assert set(int(s) // 16 for s in w.slot_mapping).isdisjoint(set(w.shared_blocks.tolist()))
 
 
+def test_prefill_large_sampled_rows():
+    """The 16 x 512-row prefill at position 3584 (2048 workgroups, the bench's
+    launch) at full size: sampled output rows against the oracle, each row
+    computed on its own as the decode query of its position (a chunk row at
+    position p attends to keys 0..p), and every row finite."""
+    w = workloads.make("prefill-large")
+    dw = DeviceWorkload(w)
+    rk, rv = run_write(dw)
+    t = torch()
+    out = empty_like_q(w.q_chunk.shape, w.dtype)
+    pws = t.empty(max(1, pkv.prefill_chunk_workspace_bytes(w.num_chunks, w.q_chunk.shape[1], w.num_q_heads,
+                                                           w.num_kv_heads, w.head_dim, w.chunk_tables.shape[1])),
+                  dtype=t.uint8, device=device())
+    pkv.paged_attn_prefill_chunk_ws(dw.q_chunk, dw.chunk_start, dw.k_cache, dw.v_cache, dw.chunk_tables,
+                                    dw.chunk_lens, float(w.scale), out, workspace=pws)
+    t.cuda.synchronize()
+    got = values(out)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(7)
+    rows = [(c, r) for c in range(w.num_chunks) for r in (0, 127, 128, 511)]
+    rows += [(int(c), int(r)) for c, r in zip(rng.integers(0, w.num_chunks, 16), rng.integers(0, 512, 16))]
+    for c, r in rows:
+        pos = int(w.chunk_start[c]) + r
+        ref = oracle.decode(w.q_chunk[c, r][None], rk, rv, w.chunk_tables[c][None],
+                            np.array([pos + 1], dtype=np.int32), w.scale, w.dtype)
+        check_attn(got[c, r][None], ref, w.dtype, f"prefill-large chunk {c} row {r}")
+
+
 # ------------------------------------------------------------------ decode shapes and edges
 
 def small(dtype, hq, hkv, d, lens, seed=1, **kw):
