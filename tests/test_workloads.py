@@ -34,7 +34,7 @@ def test_tiny_config_shape():
     assert w.scale == np.float32(0.125)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2, 3, "spec-verify-b8", "prefill-large"])
 def test_tables_slots_and_poison(cfg):
     w = workloads.make(cfg)
     bs = 16
@@ -77,6 +77,17 @@ def test_mixed_step_chunks():
     assert list(w.chunk_context_lens) == [512, 2048]
     assert w.q_chunk.shape == (2, 512, 32, 128)
     assert len(w.slot_mapping) == 48 + 1024
+
+
+def test_prefill_large_chunks():
+    w = workloads.make("prefill-large")
+    assert w.num_seqs == 0 and w.num_chunks == 16
+    assert (w.chunk_start == 3584).all() and (w.chunk_context_lens == 4096).all()
+    assert w.q_chunk.shape == (16, 512, 32, 128)
+    assert len(w.slot_mapping) == 16 * 512
+    # 4 D Hq per causal (row, key) pair: 16 chunks of 512 rows at positions 3584..4095
+    assert accounting.prefill_flops(w.chunk_start, w.chunk_context_lens, 32, 128) == \
+        4 * 128 * 32 * 16 * (3584 * 512 + 512 * 513 // 2)
 
 
 def test_bf16_rounding_nearest_even():
