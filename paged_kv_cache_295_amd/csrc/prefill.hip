@@ -49,13 +49,20 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kKT = 64;       // keys per tile
+// Keys per tile: 64 (four cache blocks, one per wave) or 32 (two blocks, half
+// a block per wave).
+#ifndef PKV_PREFILL_TILE_KEYS
+#define PKV_PREFILL_TILE_KEYS 64
+#endif
+constexpr int kKT = PKV_PREFILL_TILE_KEYS;
+constexpr int kNB = kKT / 32;  // 32-key blocks of the matrix products per tile
 constexpr int kMRows = 128;   // (head, row) pairs per workgroup
 constexpr int kThreads = 256;
 // Rescale slack of the online softmax, in powers of two (see the tile loop).
 constexpr float kPrefillSlack = 8.0f;
 constexpr int kWaves = kThreads / 64;
-static_assert(kKT == kWaves * 16, "one cache block per wave and tile");
+constexpr int kRowsPerWave = kKT / kWaves;  // key rows each wave loads per tile
+static_assert(kKT == 64 || kKT == 32, "tiles of 64 or 32 keys");
 
 // Two LDS stages (64 KiB per workgroup at head_dim 128) and registers kept
 // to two waves per SIMD let two workgroups share a compute unit, so one
@@ -65,7 +72,7 @@ static_assert(kKT == kWaves * 16, "one cache block per wave and tile");
 // mixed-step chunks 52 us against 60 us, the 64-sequence verify pass 144 us
 // against 198 us.
 #ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 2
+#define PKV_PREFILL_STAGES (PKV_PREFILL_TILE_KEYS == 32 ? 4 : 2)
 #endif
 // Waves per SIMD the register allocation must allow.
 #ifndef PKV_PREFILL_WAVES_PER_SIMD
@@ -95,12 +102,13 @@ struct PrefillShape {
   static constexpr int kTileBytes = kKT * kRowBytes;     // one K or V tile
   static constexpr int kStageBytes = 2 * kTileBytes;     // K then V
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one direct-to-LDS load fills
-  static constexpr int kLoadsPerWave = 16 / kRowsPerLoad;  // per matrix, for the wave's 16 rows
+  static constexpr int kLoadsPerWave = kRowsPerWave / kRowsPerLoad;  // per matrix, for the wave's rows
   static constexpr int kDW = 2 * kLoadsPerWave;          // direct-to-LDS loads per wave and tile
   static constexpr int kNS = PKV_PREFILL_STAGES;         // LDS stages
   static constexpr int kKSteps = D / 16;                 // QK^T steps of 16 head dims
   static constexpr int kND = D / 32;                     // PV output blocks of 32 head dims
   static_assert(kRowsPerLoad * kRC == 64, "one load covers whole rows");
+  static_assert(kLoadsPerWave >= 1, "a wave's rows fill whole loads");
   static_assert((kNS - 2) * kDW < 64, "vmcnt is six bits");
   __host__ __device__ static constexpr int vswz(int key) {
     return PKV_PREFILL_VSWZ == 1 ? (2 * key) % kRC
@@ -322,7 +330,9 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   int goff[S::kLoadsPerWave], goffv[S::kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < S::kLoadsPerWave; ++i) {
-    const int r = i * S::kRowsPerLoad + lane / RC;  // the wave's 16 rows start at a multiple of 16
+    // row within the cache block; the wave's rows sit at the same place modulo
+    // 16 in the LDS tile, where the swizzle is taken
+    const int r = (wave % (16 / kRowsPerWave)) * kRowsPerWave + i * S::kRowsPerLoad + lane / RC;
     goff[i] = r * RB + (((lane % RC) ^ (r % RC)) * 16);
     goffv[i] = r * RB + (((lane % RC) ^ S::vswz(r)) * 16);
   }
@@ -330,7 +340,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   // read block 0 (their rows are never used: K rows past the keys are masked,
   // and the V rows of the last tile past the keys are zeroed in LDS).
   auto table_entry = [&](int kt) -> int {
-    const int jb = kt * kWaves + wave;
+    const int jb = kt * (kKT / kBlock) + wave * kRowsPerWave / kBlock;
     int p = jb < nblk ? table[jb] : 0;
     if (p < 0 || p >= a.num_blocks) {
       local_bad = 1;
@@ -339,7 +349,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     return p;
   };
   auto issue = [&](int kt, int p) {  // direct-to-LDS loads of this wave's rows of tile kt (block p)
-    char* kdst = smem + (kt % NS) * S::kStageBytes + wave * 16 * RB;
+    char* kdst = smem + (kt % NS) * S::kStageBytes + wave * kRowsPerWave * RB;
     const int64_t boff = (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
     const char* kb = kc + boff;
     const char* vb = vc + boff;
@@ -388,12 +398,12 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   const bool wave_active = __builtin_amdgcn_ballot_w64(row_ok) != 0;
 
   // S^T = K Q^T for the tile whose K rows sit at LDS byte address kbase.
-  auto scores = [&](int kbase, f32x16_t (&st)[2]) {
+  auto scores = [&](int kbase, f32x16_t (&st)[kNB]) {
     int kb[S::kKSteps];
 #pragma unroll
     for (int kk = 0; kk < S::kKSteps; ++kk) kb[kk] = kbase + koff[kk];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[nb][v] = 0.0f;
       u32x4_t kv[S::kKSteps];
@@ -409,12 +419,12 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   // The online softmax of tile kt's scores and O^T += V^T P^T with its V rows
   // at LDS byte address vbase.  MASK: the tile holds keys past some row's
   // position (diagonal tiles).
-  auto finish = [&](auto mask_tag, int kt, f32x16_t (&st)[2], int vbase) {
+  auto finish = [&](auto mask_tag, int kt, f32x16_t (&st)[kNB], int vbase) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // scale, causal mask (select, diagonal tiles only), row max over this lane and lane ^ 32
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float x = st[nb][v] * sl2;
@@ -441,10 +451,10 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     }
     const float mn = m_run;
 
-    uint32_t pk[2][8];
+    uint32_t pk[kNB][8];
     float ps = 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float p0 = fast_exp2(st[nb][2 * u] - mn);
@@ -455,7 +465,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     l_run += ps;
 
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bf16x8_t bop = as_bf16x8(pk[nb][4 * s], pk[nb][4 * s + 1], pk[nb][4 * s + 2], pk[nb][4 * s + 3]);
@@ -514,7 +524,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     const int sbase = smem_base + (kt % NS) * S::kStageBytes;
     if constexpr (decltype(mask_tag)::value) zero_tail(kt, smem + (kt % NS) * S::kStageBytes + TB);
     if (!wave_active) return;
-    f32x16_t st[2];
+    f32x16_t st[kNB];
     scores(sbase, st);
     finish(mask_tag, kt, st, sbase + TB);
   };
