@@ -57,7 +57,8 @@ extern "C" {
 #define PKV_ERR_SHAPE (-3)       /* a size is negative/zero where it must be positive, Hq % Hkv != 0,
                                     max_context_len > 16 * max_blocks_per_seq, or index range overflow */
 #define PKV_ERR_UNSUPPORTED (-4) /* block_size != 16, or head_dim not 64 or 128 */
-#define PKV_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than the query function requires */
+#define PKV_ERR_WORKSPACE (-5)   /* workspace NULL, smaller than the query function requires, or not
+                                    16-byte aligned */
 #define PKV_ERR_HIP (-6)         /* a kernel launch failed (hipGetLastError after launch) */
 #define PKV_ERR_NO_BLOCKS (-7)   /* block bookkeeping: the free pool is empty */
 
@@ -238,8 +239,9 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *   partition_tokens  0 = balanced split, else fixed partitions of that many
  *                     tokens (a positive multiple of 16)
  *   workspace         device scratch of at least
- *                     paged_attn_decode_workspace_bytes(...) bytes (may be
- *                     NULL when that is 0); contents need no initialisation
+ *                     paged_attn_decode_workspace_bytes(...) bytes, 16-byte
+ *                     aligned (may be NULL when that is 0); contents need no
+ *                     initialisation
  *
  * Device-side contract: 0 <= context_lens[s] <= max_context_len and the first
  * ceil(context_lens[s]/16) table entries lie in [0, num_blocks).  A sequence
@@ -273,7 +275,8 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
  *   context_lens      int32 [num_seqs] (device): tokens after the prefix,
  *                     including the new one; 0 gives attention over the prefix alone
  *   workspace         device scratch of at least
- *                     paged_attn_decode_shared_prefix_workspace_bytes(...) bytes
+ *                     paged_attn_decode_shared_prefix_workspace_bytes(...) bytes,
+ *                     16-byte aligned
  *
  * Sequence s attends to prefix tokens 0 .. prefix_len-1 followed by its own
  * context_lens[s] tokens.  bfloat16 caches only (PKV_ERR_UNSUPPORTED for
@@ -320,7 +323,8 @@ int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t ch
  * paged_attn_prefill_chunk_ws -- paged_attn_prefill_chunk with a workspace:
  * the same arguments, result and device-side contract, and a caller-owned
  * device workspace of at least paged_attn_prefill_chunk_workspace_bytes(...)
- * bytes (0 means none is needed: the call then behaves as the plain one).
+ * bytes, 16-byte aligned (0 means none is needed: the call then behaves as
+ * the plain one).
  * When the batch has fewer (chunk, row tile, kv head) units than the GPU runs
  * workgroups at once, the keys of every row tile are cut into pieces spread
  * over the GPU and combined by a log-sum-exp merge, so one long row tile does
@@ -349,7 +353,7 @@ int paged_attn_prefill_chunk_ws(const void* q_chunk, int32_t num_chunks, int32_t
  * a sequence are few, so they share one row tile per kv head, and with few
  * sequences each (sequence, kv head)'s keys are cut into pieces spread over
  * the GPU.  Workspace: at least paged_attn_spec_verify_workspace_bytes(...)
- * bytes (0: none needed).
+ * bytes, 16-byte aligned (0: none needed).
  */
 size_t paged_attn_spec_verify_workspace_bytes(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq);

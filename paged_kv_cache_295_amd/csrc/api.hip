@@ -28,6 +28,12 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// A workspace the call needs must be present, large enough and 16-byte
+// aligned (the kernels read partial states with 8- and 16-byte loads).
+bool workspace_ok(const void* ws, size_t bytes, size_t need) {
+  return need == 0 || (ws != nullptr && bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 15) == 0);
+}
+
 // Balanced split (partition_tokens == 0): up to balanced_waves_max(gb) waves, each with
 // up to two partials of gb = heads_per_wave heads.
 size_t balanced_workspace(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
@@ -230,7 +236,7 @@ int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const vo
   if (max_parts64 > 0x7fffffffLL) return PKV_ERR_SHAPE;
   const size_t need = balanced ? balanced_workspace(num_q_heads, cache->num_kv_heads, cache->head_dim)
                                : partition_workspace(num_seqs, num_q_heads, cache->head_dim, max_context_len, part);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, need)) return PKV_ERR_WORKSPACE;
   // A batch whose every stream fits one wave's share of the balanced split
   // (at most as many blocks in all as the split has waves) runs one wave per
   // (sequence, head group) over its whole context: no partials, no merge
@@ -354,7 +360,7 @@ int paged_attn_decode_shared_prefix(const void* q, int32_t num_seqs, int32_t num
   const size_t pre = prefix_workspace(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim, prefix_len);
   const size_t pre_aligned = (pre + 255) / 256 * 256;
   const size_t need = pre_aligned + balanced_workspace(num_q_heads, cache->num_kv_heads, cache->head_dim);
-  if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, need)) return PKV_ERR_WORKSPACE;
   const float sl2 = scale * kLog2eHost;
   char* ws = reinterpret_cast<char*>(workspace);
   float* pre_o = reinterpret_cast<float*>(ws);
@@ -492,7 +498,7 @@ int paged_attn_prefill_chunk_ws(const void* q_chunk, int32_t num_chunks, int32_t
   const ChunkSplit v = chunk_split(num_chunks, chunk_len_max, num_q_heads, cache->num_kv_heads, max_blocks_per_seq);
   const size_t need = chunk_workspace(num_chunks, chunk_len_max, num_q_heads, cache->num_kv_heads, cache->head_dim,
                                       max_blocks_per_seq);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, need)) return PKV_ERR_WORKSPACE;
   PrefillArgs a{q_chunk, out, k_cache, v_cache, block_tables, context_lens, chunk_start, num_chunks, chunk_len_max,
                 num_q_heads, cache->num_kv_heads, cache->head_dim, cache->num_blocks, max_blocks_per_seq,
                 scale * kLog2eHost};

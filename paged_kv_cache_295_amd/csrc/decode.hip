@@ -412,6 +412,32 @@ struct Segment {
   // group 0 (the other groups start empty; merge_groups combines them later).
   __device__ __forceinline__ void seed(const DecodeArgs& a, int64_t row) {
     if (tg != 0) return;
+    // One partial per row (bf16 caches, the only ones the shared-prefix call
+    // takes): the state is copied as it stands, every load of the GB rows in
+    // flight together (the general loop below waits on each row's (m, l)
+    // before it reads that row's output).
+    if (std::is_same<KV, __bf16>::value && a.init_splits == 1) {
+      static_assert(EPC % 4 == 0, "16-byte loads of the partial outputs");
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const float2 ml = *reinterpret_cast<const float2*>(a.init_ml + (row + h) * 2);
+        m[h] = ml.x;
+        l[h] = ml.y;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; e += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(a.init_o + (row + h) * D + (c * LPT + li) * EPC + e);
+            acc[h][c][e] = v.x;
+            acc[h][c][e + 1] = v.y;
+            acc[h][c][e + 2] = v.z;
+            acc[h][c][e + 3] = v.w;
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < GB; ++h) bad_block |= m[h] != m[h];
+      return;
+    }
     const int64_t split_stride = (int64_t)a.num_seqs * a.num_q_heads;
 #pragma unroll
     for (int h = 0; h < GB; ++h) {

@@ -261,6 +261,29 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
   const int lane = __lane_id();
   M = -__builtin_inff();
   nan = false;
+  if (n <= kWave) {
+    // one 8-byte load of (m, l) per lane serves both the max and the weights
+    float m = -__builtin_inff(), l = 0.0f;
+    if (lane < n) {
+      const float2 v = *reinterpret_cast<const float2*>(part_ml + (row0 + lane * stride) * 2);
+      m = v.x;
+      l = v.y;
+    }
+    nan = __builtin_amdgcn_ballot_w64(m != m) != 0;
+    M = wave_max(m);
+    const float f = lane < n ? fast_exp2(m - M) : 0.0f;
+    lam = wave_sum(f * l);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+#pragma unroll 4
+    for (int j = 0; j < n; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+      const float* src = part_o + (row0 + (int64_t)j * stride) * D + lane;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = fmaf(fj, src[e * kWave], o[e]);
+    }
+    return;
+  }
   for (int p0 = 0; p0 < n; p0 += kWave) {
     const int p = p0 + lane;
     const float m = p < n ? part_ml[(row0 + p * stride) * 2] : -__builtin_inff();

@@ -94,6 +94,9 @@ def test_decode_validation(lib):
     assert decode(lib, d, maxb=256, maxlen=4096, part=0) == WS
     need0 = lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 4096, 0)
     assert decode(lib, d, maxb=256, maxlen=4096, part=0, ws=FAKE, wsb=need0 - 1) == WS
+    # a workspace must be 16-byte aligned (the kernels read partial states with 16-byte loads)
+    assert decode(lib, d, maxb=256, maxlen=4096, part=0, ws=ctypes.c_void_p(0x1004), wsb=need0) == WS
+    assert decode(lib, d, maxb=256, maxlen=4096, part=256, ws=ctypes.c_void_p(0x1008), wsb=need) == WS
     assert decode(lib, d, maxb=1 << 27, maxlen=64) == SHAPE
 
 
@@ -156,6 +159,7 @@ def test_shared_prefix_validation(lib):
     assert need > lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 0)  # + the prefix partials
     assert shared(lib, d, wsb=need - 1) == WS
     assert shared(lib, d, ws=None) == WS
+    assert shared(lib, d, ws=ctypes.c_void_p(0x1004), wsb=need) == WS
     # no prefix: just the balanced decode's workspace
     assert lib.paged_attn_decode_shared_prefix_workspace_bytes(2, 32, 8, 128, 0) == \
         lib.paged_attn_decode_workspace_bytes(2, 32, 8, 128, 64, 0)
@@ -224,6 +228,7 @@ def test_spec_verify_validation_and_workspace(lib):
     need = lib.paged_attn_spec_verify_workspace_bytes(8, 5, 32, 8, 128, 257)
     assert need == 13 * 8 * 5 * 32 * 130 * 4
     assert v(B=8, wsb=need - 1) == WS
+    assert v(B=8, ws=ctypes.c_void_p(0x1004), wsb=need) == WS
     # one piece covers the table: no workspace
     assert lib.paged_attn_spec_verify_workspace_bytes(2, 5, 32, 8, 128, 16) == 0
     assert lib.paged_attn_spec_verify_workspace_bytes(2, 5, 12, 8, 128, 16) == 0
