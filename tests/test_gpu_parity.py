@@ -388,7 +388,8 @@ def test_spec_verify_split_bad_sequence_gives_nan():
 
 
 WS_CASES = PREFILL_CASES[:6] + [("bf16", 32, 8, 128, [(1000, 300)]),       # 80 units: keys split
-                                 ("bf16", 64, 8, 128, [(2000, 100), (0, 5)])]  # split, and a chunk in one piece
+                                 ("bf16", 64, 8, 128, [(2000, 100), (0, 5)]),  # split, and a chunk in one piece
+                                 ("bf16", 8, 1, 128, [(20000, 5)])]  # one unit: 79 pieces (more than a wave's lanes)
 
 
 @pytest.mark.parametrize("case", WS_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}-{c[3]}-{len(c[4])}ch")
@@ -601,6 +602,7 @@ SHARED_CASES = [
     (64, 8, 128, 64, [1, 4000, 17, 2]),               # G = 8
     (8, 8, 64, 3, [5, 100, 0, 64]),                   # G = 1, D = 64
     (32, 8, 128, 128, [int(x) for x in np.random.default_rng(3).integers(1, 600, size=300)]),  # 300 seqs
+    (8, 1, 128, 320, [3, 40]),                        # one row tile: 80 prefix pieces (more than a wave's lanes)
 ]
 
 
