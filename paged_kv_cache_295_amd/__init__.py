@@ -248,7 +248,8 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     max_context_len: host-side bound on context_lens (defaults to the block
     table's capacity, 16 * block_tables.shape[1]).  partition_tokens: 0 for the
     balanced split, else fixed partitions of that many tokens.  workspace:
-    optional uint8 device tensor; allocated here when needed and not given.
+    optional uint8 device tensor (16-byte aligned, as torch allocations are);
+    allocated here when needed and not given.
     """
     lib = load_library()
     _same_dtype(q, out, k_cache, v_cache)
