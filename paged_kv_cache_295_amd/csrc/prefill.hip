@@ -348,17 +348,35 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     }
     return p;
   };
+  // When a chunk's rows fit one row tile (the speculative-verify rows), every
+  // K/V tile is read by this workgroup alone: the loads carry the non-temporal
+  // hint (verify of 64 x 5 rows 112.9 -> 100.0 us, 157 -> 103 us with cold
+  // caches).  Row tiles that share their keys through L2 (prefill chunks, the
+  // prefix) keep the default policy: with the hint the large prefill took
+  // 570 us against 542.
+  const bool stream_kv = !PREFIX && a.chunk_len_max * G <= kMRows;
   auto issue = [&](int kt, int p) {  // direct-to-LDS loads of this wave's rows of tile kt (block p)
     char* kdst = smem + (kt % NS) * S::kStageBytes + wave * kRowsPerWave * RB;
     const int64_t boff = (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
     const char* kb = kc + boff;
     const char* vb = vc + boff;
+    constexpr int kNT = 2;  // cache-policy bit of the non-temporal hint
+    if (stream_kv) {
 #pragma unroll
-    for (int i = 0; i < S::kLoadsPerWave; ++i) {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + goff[i]),
-                                       (__attribute__((address_space(3))) void*)(kdst + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + goffv[i]),
-                                       (__attribute__((address_space(3))) void*)(kdst + TB + i * 1024), 16, 0, 0);
+      for (int i = 0; i < S::kLoadsPerWave; ++i) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + goff[i]),
+                                         (__attribute__((address_space(3))) void*)(kdst + i * 1024), 16, 0, kNT);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + goffv[i]),
+                                         (__attribute__((address_space(3))) void*)(kdst + TB + i * 1024), 16, 0, kNT);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::kLoadsPerWave; ++i) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + goff[i]),
+                                         (__attribute__((address_space(3))) void*)(kdst + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + goffv[i]),
+                                         (__attribute__((address_space(3))) void*)(kdst + TB + i * 1024), 16, 0, 0);
+      }
     }
   };
 
