@@ -188,11 +188,31 @@ __global__ __launch_bounds__(256) void kv_copy_blocks_kernel(uint4* __restrict__
     const uint4* vs = v_cache + (int64_t)src * block_chunks;
     uint4* kd = k_cache + (int64_t)dst * block_chunks;
     uint4* vd = v_cache + (int64_t)dst * block_chunks;
-    for (int64_t j = threadIdx.x; j < block_chunks; j += blockDim.x) {
-      const uint4 a = ks[j];
-      const uint4 b = vs[j];
-      kd[j] = a;
-      vd[j] = b;
+    // Every load of a thread's chunks is in flight before its stores, and the
+    // stores carry the non-temporal hint (the copied blocks are not read again
+    // in the call).  512 pairs of 2 x 32 KiB: 9.9 us against 11.2 us for one
+    // load pair per iteration with plain stores; non-temporal loads as well
+    // took 13.4 us.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kUnroll = 8;
+    for (int64_t j0 = threadIdx.x; j0 < block_chunks; j0 += (int64_t)blockDim.x * kUnroll) {
+      u32x4 a[kUnroll], b[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t j = j0 + (int64_t)u * blockDim.x;
+        if (j < block_chunks) {
+          a[u] = *reinterpret_cast<const u32x4*>(ks + j);
+          b[u] = *reinterpret_cast<const u32x4*>(vs + j);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t j = j0 + (int64_t)u * blockDim.x;
+        if (j < block_chunks) {
+          __builtin_nontemporal_store(a[u], reinterpret_cast<u32x4*>(kd + j));
+          __builtin_nontemporal_store(b[u], reinterpret_cast<u32x4*>(vd + j));
+        }
+      }
     }
   }
 }
