@@ -262,7 +262,16 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
   M = -__builtin_inff();
   nan = false;
   if (n <= kWave) {
-    // one 8-byte load of (m, l) per lane serves both the max and the weights
+    // one 8-byte load of (m, l) per lane serves both the max and the weights;
+    // the outputs of the first kPre partials are loaded at the same time
+    constexpr int kPre = 8;
+    float pre[kPre][PER];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {  // past the n-th, partial 0 again (in bounds, unused)
+      const float* src = part_o + (row0 + (int64_t)(j < n ? j : 0) * stride) * D + lane;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) pre[j][e] = src[e * kWave];
+    }
     float m = -__builtin_inff(), l = 0.0f;
     if (lane < n) {
       const float2 v = *reinterpret_cast<const float2*>(part_ml + (row0 + lane * stride) * 2);
@@ -275,8 +284,16 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
     lam = wave_sum(f * l);
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      if (j < n) {
+        const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] = fmaf(fj, pre[j][e], o[e]);
+      }
+    }
 #pragma unroll 4
-    for (int j = 0; j < n; ++j) {
+    for (int j = kPre; j < n; ++j) {
       const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
       const float* src = part_o + (row0 + (int64_t)j * stride) * D + lane;
 #pragma unroll
