@@ -41,10 +41,10 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 # only for the decode kernel sources it was measured on: reported as null once
 # their hash differs.
 TRAFFIC = {
-    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 530001568, "write_bytes": 3422291,
-                                        "sources_sha256": "7472615cd323fe1afb04efb18c58e6ad700bbbe6a2bfd188b2cf5f5f98d61c90"},
-    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 285126091, "write_bytes": 5462587,
-                                      "sources_sha256": "7472615cd323fe1afb04efb18c58e6ad700bbbe6a2bfd188b2cf5f5f98d61c90"},
+    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 530040320, "write_bytes": 3422147,
+                                        "sources_sha256": "2262b5bf93b717dec9a5f08df814efd21811532944d60e19fcd16b1bde5ecf7d"},
+    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 284962795, "write_bytes": 5462576,
+                                      "sources_sha256": "2262b5bf93b717dec9a5f08df814efd21811532944d60e19fcd16b1bde5ecf7d"},
 }
 CSRC = os.path.join(ROOT, "paged_kv_cache_295_amd", "csrc")
 DECODE_SOURCES = ("decode.hip", "pkv_device.hpp", "pkv_internal.hpp")
