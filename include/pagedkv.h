@@ -219,6 +219,31 @@ int paged_block_release(const int32_t* table, int32_t num_table_blocks, int32_t*
  * needs for these sizes (0 if none).
  */
 int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads);
+
+/*
+ * paged_attn_lse_merge -- the log-sum-exp merge of split-context partials on
+ * its own: for every row r, with partials p = 0 .. num_parts-1,
+ *     M = max_p m_p,   out[r] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
+ * which is softmax(x) V over the union of the parts' keys ("Part 47",
+ * section 2.1, for the softmax; splitting a context into parts is this
+ * library's, the pages do not describe it).  It is the merge the decode calls
+ * run after fixed partitions, exported so that it can be checked alone.
+ *
+ *   part_o    float32 [num_rows][num_parts][head_dim]: o_p = sum_t 2^(y_t - m_p) v_t,
+ *             unnormalised, over part p's keys t (y_t = score * log2(e))
+ *   part_ml   float32 [num_rows][num_parts][2]: (m_p, l_p) with m_p >= max_t y_t of
+ *             the part, in log2 units, and l_p = sum_t 2^(y_t - m_p)
+ *   out       [num_rows][head_dim], out_dtype PKV_DTYPE_F32 or PKV_DTYPE_BF16
+ *             (bf16 rounded to nearest even)
+ *
+ * A part with no keys is (m_p, 0, 0) for any m_p that is not NaN (-inf
+ * included, as long as some part of the row has a finite m_p).  A row with a
+ * NaN m_p gets NaN; a row whose parts are all empty is undefined.  part_o and
+ * part_ml must be 16-byte aligned (PKV_ERR_SHAPE otherwise).  num_rows == 0
+ * is a no-op.
+ */
+int paged_attn_lse_merge(const float* part_o, const float* part_ml, int64_t num_rows, int32_t num_parts,
+                         int32_t head_dim, int32_t out_dtype, void* out, void* hip_stream);
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_context_len, int32_t partition_tokens);
 
@@ -318,7 +343,6 @@ int paged_attn_prefill_chunk(const void* q_chunk, int32_t num_chunks, int32_t ch
                              int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
                              void* out, void* hip_stream);
 
-/* Human-readable name of a status code (static storage). */
 /*
  * paged_attn_prefill_chunk_ws -- paged_attn_prefill_chunk with a workspace:
  * the same arguments, result and device-side contract, and a caller-owned
@@ -363,11 +387,12 @@ int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, in
                            const int32_t* context_lens, float scale, void* out, void* workspace,
                            size_t workspace_bytes, void* hip_stream);
 
+/* Human-readable name of a status code (static storage). */
 const char* pkv_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION ((1 << 16) | 5)
+#define PKV_ABI_VERSION ((1 << 16) | 6)
 
 #ifdef __cplusplus
 }

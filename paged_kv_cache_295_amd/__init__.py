@@ -19,7 +19,7 @@ __all__ = [
     "paged_attn_decode_shared_prefix", "shared_prefix_workspace_bytes", "paged_kv_copy_blocks", "BlockPool",
     "paged_kv_write_fp8", "paged_attn_decode_fp8", "paged_kv_copy_blocks_fp8",
     "paged_attn_spec_verify", "spec_verify_workspace_bytes", "paged_attn_prefill_chunk_ws",
-    "prefill_chunk_workspace_bytes",
+    "prefill_chunk_workspace_bytes", "paged_attn_lse_merge",
 ]
 
 BLOCK_SIZE = 16
@@ -99,6 +99,8 @@ def load_library():
     lib.paged_attn_spec_verify_workspace_bytes.restype = sz
     lib.paged_attn_spec_verify.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp, sz, vp]
     lib.paged_attn_spec_verify.restype = ctypes.c_int
+    lib.paged_attn_lse_merge.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
+    lib.paged_attn_lse_merge.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -119,6 +121,23 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.bfloat16:
         return PKV_DTYPE_BF16
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _on_one_gpu(*tensors):
+    """Every tensor argument must live on one GPU: the kernels dereference these
+    addresses, and a host tensor's address read on the GPU is a wild pointer.
+    Checked before the library is called, so a misplaced tensor never reaches a kernel."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"tensor arguments must be on the GPU, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensor arguments must be on one GPU, got {dev} and {t.device}")
+    return dev
 
 
 def _ptr(t) -> int:
@@ -176,6 +195,7 @@ def _check(status: int, what: str):
 
 def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
     """Store row i of k/v ([T, Hkv, D]) at cache slot slot_mapping[i] (int32 [T])."""
+    _on_one_gpu(k, v, slot_mapping, k_cache, v_cache)
     lib = load_library()
     _same_dtype(k, v, k_cache, v_cache)
     desc = _cache_desc(k_cache)
@@ -190,6 +210,7 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
 
 def paged_kv_copy_blocks(src_blocks, dst_blocks, k_cache, v_cache, stream=None):
     """Copy block src_blocks[i] to block dst_blocks[i] in both caches (int32 [N] each)."""
+    _on_one_gpu(src_blocks, dst_blocks, k_cache, v_cache)
     lib = load_library()
     _same_dtype(k_cache, v_cache)
     desc = _cache_desc(k_cache)
@@ -204,6 +225,7 @@ def paged_kv_copy_blocks(src_blocks, dst_blocks, k_cache, v_cache, stream=None):
 
 def paged_kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream=None):
     """Quantise row i of k/v ([T, Hkv, D], bf16 or f32) into E4M3 codes + scales at slot slot_mapping[i]."""
+    _on_one_gpu(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale)
     lib = load_library()
     desc = _fp8_desc(k_cache, v_cache, k_scale, v_scale)
     if k.dtype != v.dtype:
@@ -220,6 +242,7 @@ def paged_kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, s
 
 def paged_kv_copy_blocks_fp8(src_blocks, dst_blocks, k_cache, v_cache, k_scale, v_scale, stream=None):
     """Copy block src_blocks[i] to dst_blocks[i]: codes of both caches and their scales."""
+    _on_one_gpu(src_blocks, dst_blocks, k_cache, v_cache, k_scale, v_scale)
     lib = load_library()
     desc = _fp8_desc(k_cache, v_cache, k_scale, v_scale)
     if src_blocks.dim() != 1 or dst_blocks.shape != src_blocks.shape:
@@ -251,6 +274,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     optional uint8 device tensor (16-byte aligned, as torch allocations are);
     allocated here when needed and not given.
     """
+    _on_one_gpu(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
     lib = load_library()
     _same_dtype(q, out, k_cache, v_cache)
     desc = _cache_desc(k_cache)
@@ -278,6 +302,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
 def paged_attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, out,
                           max_context_len=None, partition_tokens=0, workspace=None, stream=None):
     """paged_attn_decode over an E4M3 cache with per-(slot, kv head) scales; q and out bfloat16."""
+    _on_one_gpu(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out, workspace)
     lib = load_library()
     torch = _torch()
     desc = _fp8_desc(k_cache, v_cache, k_scale, v_scale)
@@ -313,6 +338,7 @@ def paged_attn_decode_shared_prefix(q, k_cache, v_cache, prefix_blocks, block_ta
                                     workspace=None, stream=None):
     """Decode for sequences that share the prefix held in prefix_blocks (int32 [P]; P*16 tokens):
     sequence s attends to the prefix and then to its own context_lens[s] tokens in block_tables[s]."""
+    _on_one_gpu(q, k_cache, v_cache, prefix_blocks, block_tables, context_lens, out, workspace)
     lib = load_library()
     _same_dtype(q, out, k_cache, v_cache)
     desc = _cache_desc(k_cache)
@@ -340,6 +366,7 @@ def paged_attn_decode_shared_prefix(q, k_cache, v_cache, prefix_blocks, block_ta
 def paged_attn_prefill_chunk(q_chunk, chunk_start, k_cache, v_cache, block_tables, context_lens, scale, out,
                              stream=None):
     """Causal attention of each chunk's rows (q_chunk [Nc, Cmax, Hq, D]) over its cached context."""
+    _on_one_gpu(q_chunk, chunk_start, k_cache, v_cache, block_tables, context_lens, out)
     lib = load_library()
     _same_dtype(q_chunk, out, k_cache, v_cache)
     desc = _cache_desc(k_cache)
@@ -425,6 +452,7 @@ def spec_verify_workspace_bytes(num_seqs, rows_max, num_q_heads, num_kv_heads, h
 
 def _chunks_with_workspace(fn, size_fn, what, q, starts, k_cache, v_cache, block_tables, context_lens, scale, out,
                            workspace, stream):
+    _on_one_gpu(q, starts, k_cache, v_cache, block_tables, context_lens, out, workspace)
     lib = load_library()
     torch = _torch()
     _same_dtype(q, out, k_cache, v_cache)
@@ -463,3 +491,20 @@ def paged_attn_spec_verify(q, row_start, k_cache, v_cache, block_tables, context
     return _chunks_with_workspace("paged_attn_spec_verify", spec_verify_workspace_bytes, "paged_attn_spec_verify",
                                   q, row_start, k_cache, v_cache, block_tables, context_lens, scale, out, workspace,
                                   stream)
+
+
+def paged_attn_lse_merge(part_o, part_ml, out, stream=None):
+    """Log-sum-exp merge of split-context partials: part_o float32 [R, P, D] (unnormalised
+    outputs), part_ml float32 [R, P, 2] ((max in log2 units, sum of 2^(y - max))), out [R, D]
+    float32 or bfloat16 = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p."""
+    _on_one_gpu(part_o, part_ml, out)
+    lib = load_library()
+    torch = _torch()
+    if part_o.dtype != torch.float32 or part_ml.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if part_o.dim() != 3 or part_ml.shape != part_o.shape[:2] + (2,) or out.shape != (part_o.shape[0], part_o.shape[2]):
+        raise ValueError("part_o [R, P, D], part_ml [R, P, 2], out [R, D]")
+    R, P, D = part_o.shape
+    st = lib.paged_attn_lse_merge(_ptr(part_o), _ptr(part_ml), R, P, D, _dtype_code(out), _ptr(out), _stream(stream))
+    _check(st, "paged_attn_lse_merge")
+    return out

@@ -199,6 +199,19 @@ int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads)
   return balanced_waves(heads_per_wave(num_q_heads / num_kv_heads), PKV_DTYPE_BF16);
 }
 
+int paged_attn_lse_merge(const float* part_o, const float* part_ml, int64_t num_rows, int32_t num_parts,
+                         int32_t head_dim, int32_t out_dtype, void* out, void* hip_stream) {
+  if (num_rows < 0) return PKV_ERR_SHAPE;
+  if (num_rows == 0) return PKV_OK;
+  if (!part_o || !part_ml || !out) return PKV_ERR_NULL;
+  if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (num_parts <= 0 || num_rows > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (((reinterpret_cast<uintptr_t>(part_o) | reinterpret_cast<uintptr_t>(part_ml)) & 15) != 0) return PKV_ERR_SHAPE;
+  return from_hip(launch_lse_merge(part_o, part_ml, num_rows, num_parts, head_dim, out_dtype, out,
+                                   as_stream(hip_stream)));
+}
+
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||

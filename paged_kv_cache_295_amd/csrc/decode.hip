@@ -646,7 +646,9 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(const DecodeArgs a
 
 // Log-sum-exp merge of the partitions of every (query row, query head) whose
 // context spans more than one partition.  One wave per (row, head); lane k
-// owns output dims k, k + 64, ...
+// owns output dims k, k + 64, ...  The partitions of a row are consecutive in
+// the workspace ([row][head][max_parts]), so merge_partials reads them with
+// stride 1, every (m, l) load in flight at once.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   constexpr int PER = D / kWave;
@@ -658,27 +660,57 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   const int P = a.partition_tokens;
   if (ri.skip || ri.bad || ri.keys <= P) return;
   const int nparts = (ri.keys + P - 1) / P;
-  const int64_t base = (row * a.num_q_heads + h) * (int64_t)a.max_parts;
-  const float* ml = a.part_ml + base * 2;
-
-  float M = -__builtin_inff();
-  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
-
-  float lam = 0.0f, o[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.0f;
-  const float* po = a.part_o + base * D;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = fast_exp2(ml[2 * p] - M);
-    lam = fmaf(w, ml[2 * p + 1], lam);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = fmaf(w, po[(int64_t)p * D + lane + k * kWave], o[k]);
-  }
-  const float inv = 1.0f / lam;
+  float o[PER], M, lam;
+  bool nan;
+  merge_partials<D>(a.part_o, a.part_ml, (row * a.num_q_heads + h) * (int64_t)a.max_parts, 1, nparts, o, M, lam,
+                    nan);
+  const float inv = nan ? __builtin_nanf("") : 1.0f / lam;
   T* outp = reinterpret_cast<T*>(a.out) + (row * a.num_q_heads + h) * (int64_t)D;
 #pragma unroll
   for (int k = 0; k < PER; ++k) outp[lane + k * kWave] = (T)(o[k] * inv);
+}
+
+// The merge on its own (paged_attn_lse_merge): row r's parts partials at
+// [r][p] of part_o ([rows][parts][D]) and part_ml ([rows][parts][2]), the
+// normalised result to out [rows][D].  One wave per row.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void lse_merge_kernel(const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_ml, int64_t rows, int parts,
+                                                       T* __restrict__ out) {
+  constexpr int PER = D / kWave;
+  const int lane = __lane_id();
+  const int64_t row = blockIdx.x;
+  if (row >= rows) return;
+  float o[PER], M, lam;
+  bool nan;
+  merge_partials<D>(part_o, part_ml, row * parts, 1, parts, o, M, lam, nan);
+  const float inv = nan ? __builtin_nanf("") : 1.0f / lam;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) out[row * D + lane + k * kWave] = (T)(o[k] * inv);
+}
+
+template <typename T>
+static hipError_t launch_lse_merge_typed(const float* part_o, const float* part_ml, int64_t rows, int parts,
+                                         int head_dim, void* out, hipStream_t stream) {
+  T* o = reinterpret_cast<T*>(out);
+  if (head_dim == 64)
+    hipLaunchKernelGGL((lse_merge_kernel<T, 64>), dim3((unsigned)rows), dim3(64), 0, stream, part_o, part_ml, rows,
+                       parts, o);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((lse_merge_kernel<T, 128>), dim3((unsigned)rows), dim3(64), 0, stream, part_o, part_ml, rows,
+                       parts, o);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int64_t rows, int parts, int head_dim,
+                            int out_dtype, void* out, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (rows > 0x7fffffffLL || parts <= 0) return hipErrorInvalidValue;
+  if (out_dtype == 0) return launch_lse_merge_typed<float>(part_o, part_ml, rows, parts, head_dim, out, stream);
+  if (out_dtype == 1) return launch_lse_merge_typed<__bf16>(part_o, part_ml, rows, parts, head_dim, out, stream);
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- balanced split

@@ -101,6 +101,10 @@ hipError_t launch_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* sr
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefix_mfma(const PrefillArgs& a, hipStream_t stream);
+// The log-sum-exp merge on its own: rows x parts partials ([row][part]) into
+// out [rows][head_dim] of out_dtype (0 float32, 1 bfloat16).
+hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int64_t rows, int parts, int head_dim,
+                            int out_dtype, void* out, hipStream_t stream);
 // Merges the splits partials of each of `rows` rows into the first split's slot.
 hipError_t launch_prefix_merge(float* part_o, float* part_ml, int64_t rows, int splits, int head_dim,
                                hipStream_t stream);

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == (1 << 16) | 5
+    assert lib.pkv_abi_version() == (1 << 16) | 6
 
 
 def test_status_strings(lib):
@@ -249,3 +249,56 @@ def test_prefill_chunk_ws_workspace(lib):
     assert c(n=0) == OK
     assert lib.paged_attn_spec_verify_workspace_bytes(8, 5, 32, 8, 128, 257) == \
         lib.paged_attn_prefill_chunk_workspace_bytes(8, 5, 32, 8, 128, 257)
+
+
+def test_lse_merge_validation(lib):
+    m = lib.paged_attn_lse_merge
+    assert m(None, None, 0, 4, 128, 1, None, None) == OK          # no rows: no-op
+    assert m(FAKE, FAKE, -1, 4, 128, 1, FAKE, None) == SHAPE
+    assert m(None, FAKE, 3, 4, 128, 1, FAKE, None) == NULL
+    assert m(FAKE, FAKE, 3, 4, 128, 2, FAKE, None) == DTYPE        # fp8 outputs do not exist
+    assert m(FAKE, FAKE, 3, 4, 96, 1, FAKE, None) == UNSUP
+    assert m(FAKE, FAKE, 3, 0, 128, 1, FAKE, None) == SHAPE
+    assert m(FAKE, FAKE, 1 << 31, 4, 128, 1, FAKE, None) == SHAPE
+    assert m(ctypes.c_void_p(0x1008), FAKE, 3, 4, 128, 1, FAKE, None) == SHAPE  # partials not 16-byte aligned
+
+
+class _NoCalls:
+    """Stands in for the library: any call is a failure of the test."""
+
+    def __getattr__(self, name):
+        raise AssertionError(f"the library was called ({name}) with a tensor off the GPU")
+
+
+def test_binding_rejects_host_tensors_before_any_call(monkeypatch):
+    """A host tensor's address handed to a kernel would be a wild pointer on the GPU:
+    every wrapper refuses tensors that are not on the GPU before it calls the library."""
+    import torch
+    monkeypatch.setattr(pkv, "_lib", _NoCalls())
+    bf = torch.bfloat16
+    q = torch.zeros(2, 32, 128, dtype=bf)
+    kc = torch.zeros(8, 8, 16, 128, dtype=bf)
+    tab = torch.zeros(2, 4, dtype=torch.int32)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_attn_decode(q, kc, kc, tab, lens, 0.1, q.clone())
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_kv_write(q[:, :8], q[:, :8], lens, kc, kc)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_attn_prefill_chunk(q[None], lens[:1], kc, kc, tab[:1], lens[:1], 0.1, q[None].clone())
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_attn_decode_shared_prefix(q, kc, kc, lens, tab, lens, 0.1, q.clone())
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_kv_copy_blocks(lens, lens, kc, kc)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_attn_spec_verify(q[None], lens[:1], kc, kc, tab[:1], lens[:1], 0.1, q[None].clone())
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_attn_lse_merge(torch.zeros(3, 2, 128), torch.zeros(3, 2, 2), torch.zeros(3, 128))
+    u8 = torch.zeros(8, 8, 16, 128, dtype=torch.uint8)
+    sc = torch.ones(8, 8, 16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_attn_decode_fp8(q, u8, u8, sc, sc, tab, lens, 0.1, q.clone())
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_kv_write_fp8(q[:, :8], q[:, :8], lens, u8, u8, sc, sc)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.paged_kv_copy_blocks_fp8(lens, lens, u8, u8, sc, sc)

@@ -4,7 +4,8 @@ Bar: the quantising write is bit-exact (codes and scales over the whole pool,
 poisoned slots included); the block copy is bit-exact; decode over the
 quantised cache is within 2^-6 * max|V| of the oracle's float64 attention over
 the same dequantised values (the kernel rounds the probabilities and the
-output to bfloat16, 3 * 2^-9 * max|V| at most; the bar leaves a margin).
+output to bfloat16, 3 * 2^-9 * max|V| at most; the bar leaves a margin) and
+within 2^-6 row-normwise relative error (tests/tolerances.py).
 """
 import numpy as np
 import pytest
@@ -14,6 +15,7 @@ import paged_kv_cache_295_amd as pkv
 import workloads
 from oracle import fp8_cache as f8
 from tests.gpu_util import empty_like_q, to_dev, torch, values
+from tests.tolerances import FP8_REL, attn_errors, record
 from workloads import SeqSpec, build
 
 pytestmark = pytest.mark.gpu
@@ -73,7 +75,10 @@ def check_fp8(got, ref, v_codes, v_scale, tables, lens, hkv, what):
             assert err <= 2.0 ** -6 * vmax + 1e-30, f"{what}: seq {s} kv head {g}: err {err} vmax {vmax}"
             worst = max(worst, err / max(vmax, 1e-30))
     assert np.isfinite(got).all()
-    say(f"{what}: max err / max|V| = {worst:.3e}")
+    a, r = attn_errors(got, ref)
+    record(what, "fp8", a, r)
+    say(f"{what}: max err / max|V| = {worst:.3e}, max row-normwise rel err {r:.3e}")
+    assert r <= FP8_REL, f"{what}: row-normwise rel err {r}"
 
 
 def write_and_decode(w, what, partition_tokens=0):

@@ -1,8 +1,9 @@
 """GPU parity: the HIP library against the fp64 CPU oracle on the same seeded inputs.
 
-Bar: cache writes bit-exact over the whole cache (poisoned slots included);
-attention within 1e-5 max row-normwise relative error for float32 inputs and
-2e-2 max absolute error for bf16 inputs (unit-variance values, float32
+Bars (tests/tolerances.py): cache writes bit-exact over the whole cache
+(poisoned slots included); attention within 1e-5 max row-normwise relative
+error for float32 inputs; for bf16 inputs within 2e-2 max absolute error and
+5 * 2^-9 max row-normwise relative error (unit-variance values, float32
 accumulation).
 """
 import numpy as np
@@ -12,12 +13,11 @@ import oracle
 import paged_kv_cache_295_amd as pkv
 import workloads
 from tests.gpu_util import DeviceWorkload, bits, device, empty_like_q, to_dev, torch, values
+from tests.tolerances import BF16_ABS, BF16_REL, F32_REL, attn_errors, record
 from workloads import SeqSpec, build
 
 pytestmark = pytest.mark.gpu
 
-F32_REL = 1e-5
-BF16_ABS = 2e-2
 SENTINEL = -1024.0  # exact in bf16 and float32
 
 
@@ -26,14 +26,14 @@ def say(*a):
 
 
 def check_attn(got, ref, dtype, what):
+    a, r = attn_errors(got, ref)
+    record(what, dtype, a, r)
+    say(f"{what}: max abs err {a:.3e}, max row-normwise rel err {r:.3e}")
     if dtype == "f32":
-        err = oracle.max_rownorm_rel_err(got, ref)
-        say(f"{what}: max row-normwise rel err {err:.3e}")
-        assert err <= F32_REL, f"{what}: rel err {err}"
+        assert r <= F32_REL, f"{what}: rel err {r}"
     else:
-        err = oracle.max_abs_err(got, ref)
-        say(f"{what}: max abs err {err:.3e}")
-        assert err <= BF16_ABS, f"{what}: abs err {err}"
+        assert a <= BF16_ABS, f"{what}: abs err {a}"
+        assert r <= BF16_REL, f"{what}: row-normwise rel err {r}"
     assert np.isfinite(got).all()
 
 
@@ -72,6 +72,7 @@ def write_decode_prefill_vs_oracle(w, what):
     assert np.array_equal(bits(dw.k_cache), ref_k.view(bits(dw.k_cache).dtype)), f"{what}: K cache bits"
     assert np.array_equal(bits(dw.v_cache), ref_v.view(bits(dw.v_cache).dtype)), f"{what}: V cache bits"
     say(f"[{what}] write bit-exact over {ref_k.nbytes * 2 / 1e6:.1f} MB of cache")
+    ref = None
     if w.num_seqs:
         out = run_decode(dw)
         ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
@@ -85,7 +86,7 @@ def write_decode_prefill_vs_oracle(w, what):
             n = int(w.chunk_context_lens[c] - w.chunk_start[c])
             check_attn(got[c, :n], ref[c, :n], w.dtype, f"[{what}] prefill chunk {c}")
             assert (got[c, n:] == SENTINEL).all(), "rows past the chunk must not be written"
-    return dw, ref_k, ref_v
+    return dw, ref_k, ref_v, ref
 
 
 # ------------------------------------------------------------------ the five serving mixes
@@ -93,17 +94,19 @@ def write_decode_prefill_vs_oracle(w, what):
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_config_parity(cfg):
     w = workloads.make(cfg)
-    write_decode_prefill_vs_oracle(w, f"cfg{cfg}")
+    dw, _, _, ref = write_decode_prefill_vs_oracle(w, f"cfg{cfg}")
+    if cfg == 5:
+        # as the long-context batch is configured: split-context partitions of 2048 tokens (16-64 per
+        # sequence, eight query heads per wave) and the log-sum-exp merge kernel
+        check_attn(values(run_decode(dw, partition_tokens=2048)), ref, w.dtype, "[cfg5] decode, partitions of 2048")
     if cfg == 4:
         # writes never touch the shared prefix blocks
         assert set(int(s) // 16 for s in w.slot_mapping).isdisjoint(set(w.shared_blocks.tolist()))
 
 
-def test_prefill_large_sampled_rows():
-    """The 16 x 512-row prefill at position 3584 (2048 workgroups, the bench's
-    launch) at full size: sampled output rows against the oracle, each row
-    computed on its own as the decode query of its position (a chunk row at
-    position p attends to keys 0..p), and every row finite."""
+def test_prefill_large_every_row():
+    """The 16 x 512-row prefill at position 3584 (2048 workgroups, the launch the
+    benchmark times) at full size: every row of every chunk against the oracle."""
     w = workloads.make("prefill-large")
     dw = DeviceWorkload(w)
     rk, rv = run_write(dw)
@@ -116,15 +119,11 @@ def test_prefill_large_sampled_rows():
                                     dw.chunk_lens, float(w.scale), out, workspace=pws)
     t.cuda.synchronize()
     got = values(out)
-    assert np.isfinite(got).all()
-    rng = np.random.default_rng(7)
-    rows = [(c, r) for c in range(w.num_chunks) for r in (0, 127, 128, 511)]
-    rows += [(int(c), int(r)) for c, r in zip(rng.integers(0, w.num_chunks, 16), rng.integers(0, 512, 16))]
-    for c, r in rows:
-        pos = int(w.chunk_start[c]) + r
-        ref = oracle.decode(w.q_chunk[c, r][None], rk, rv, w.chunk_tables[c][None],
-                            np.array([pos + 1], dtype=np.int32), w.scale, w.dtype)
-        check_attn(got[c, r][None], ref, w.dtype, f"prefill-large chunk {c} row {r}")
+    ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale,
+                               w.dtype)
+    n = w.q_chunk.shape[1]
+    assert (w.chunk_context_lens - w.chunk_start == n).all()
+    check_attn(got, ref, w.dtype, "prefill-large, all 16 x 512 rows")
 
 
 # ------------------------------------------------------------------ decode shapes and edges
@@ -148,12 +147,26 @@ def test_decode_shapes_and_ragged_lengths(shape):
 
 
 @pytest.mark.parametrize("part", [0, 256, 512, 2048, 4096])
-def test_decode_partition_sizes(part):
-    w = small("bf16", 32, 8, 128, [3000, 5000, 17, 4097, 8192, 1], seed=3)
+@pytest.mark.parametrize("heads", [(32, 8), (64, 8)], ids=lambda h: f"{h[0]}q{h[1]}kv")
+def test_decode_partition_sizes(part, heads):
+    hq, hkv = heads
+    w = small("bf16", hq, hkv, 128, [3000, 5000, 17, 4097, 8192, 1], seed=3)
     dw = DeviceWorkload(w)
     ref_k, ref_v = run_write(dw)
     ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
-    check_attn(values(run_decode(dw, partition_tokens=part)), ref, "bf16", f"partition {part}")
+    check_attn(values(run_decode(dw, partition_tokens=part)), ref, "bf16", f"partition {part}, {heads}")
+
+
+@pytest.mark.parametrize("part", [16, 256, 1024])  # 16: up to 188 partials per row, more than a wave has lanes
+@pytest.mark.parametrize("shape", [(8, 8, 64), (32, 8, 128)], ids=lambda s: f"{s[0]}q{s[1]}kv{s[2]}")
+def test_decode_partition_sizes_f32(part, shape):
+    """float32 caches through fixed partitions and the float32 merge kernel."""
+    hq, hkv, d = shape
+    w = small("f32", hq, hkv, d, [1500, 64, 65, 3000, 1, 700], seed=17)
+    dw = DeviceWorkload(w)
+    ref_k, ref_v = run_write(dw)
+    ref = oracle.decode(w.q, ref_k, ref_v, w.block_tables, w.context_lens, w.scale, w.dtype)
+    check_attn(values(run_decode(dw, partition_tokens=part)), ref, "f32", f"f32 partition {part}, {shape}")
 
 
 def test_decode_grid_bound_above_lengths():
@@ -337,7 +350,7 @@ def test_spec_verify_parity(case):
     sequences accepted fewer) over contexts from a few tokens to a few thousand,
     through the prefill-chunk call and through the verify call (keys split)."""
     w = verify_workload(case)
-    dw, rk, rv = write_decode_prefill_vs_oracle(w, f"verify {case}")
+    dw, rk, rv, _ = write_decode_prefill_vs_oracle(w, f"verify {case}")
     out, need = run_verify(dw)
     say(f"verify call: workspace {need} bytes")
     ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale,
@@ -509,7 +522,12 @@ def test_prefill_last_row_equals_decode():
     out = t.empty_like(q)
     pkv.paged_attn_decode(q, dw.k_cache, dw.v_cache, dw.chunk_tables, dw.chunk_lens, float(w.scale), out)
     t.cuda.synchronize()
-    # different kernels (MFMA with bf16 P vs. vector path): both within tolerance of each other
+    # different kernels (matrix cores against the vector path): each meets the bar against the oracle's
+    # decode of that position, and the two stay within the absolute bar of each other
+    rk, rv = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
+    ref = oracle.decode(w.q_chunk[0, 199:200], rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale, w.dtype)
+    check_attn(values(out), ref, "bf16", "decode of the chunk's last position")
+    check_attn(pf[None], ref, "bf16", "the chunk's last row")
     assert oracle.max_abs_err(values(out)[0], pf) <= BF16_ABS
 
 
@@ -591,8 +609,8 @@ def test_shared_prefix_cfg4():
     out, own, own_lens = run_shared_prefix(dw, w, n_pre)
     ref = oracle.decode_shared_prefix(w.q, ref_k, ref_v, w.shared_blocks, own, own_lens, w.scale, w.dtype)
     check_attn(values(out), ref, "bf16", "cascade cfg4")
-    # and the same as plain decode over the full tables
-    check_attn(values(out), values(run_decode(dw)), "bf16", "cascade vs plain decode")
+    # and the plain decode over the full tables, a different kernel path, meets the same bar
+    check_attn(values(run_decode(dw)), ref, "bf16", "cfg4 plain decode over the full tables")
 
 
 SHARED_CASES = [

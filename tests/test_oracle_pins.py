@@ -378,3 +378,41 @@ def test_copy_blocks_element_loop_and_invariance():
     a = oracle.decode(q, k2, v2, np.array([[0, 7]], dtype=np.int32), np.array([30]), 0.5, "f32")
     b = oracle.decode(q, k2, v2, np.array([[10, 11]], dtype=np.int32), np.array([30]), 0.5, "f32")
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------ the comparison helpers every GPU verdict uses
+
+def test_comparison_helpers_against_hand_computed_values():
+    """max_abs_err and max_rownorm_rel_err on values worked out by hand.
+
+    Rows are the last axis.  Row 0: errors (0.5, 0, 0), largest |ref| 4 -> 0.125.
+    Row 1: errors (0, 0.05, 0), largest |ref| 0.5 -> 0.1.  Row 2: a zero
+    reference row divides by 1 (its relative error is its absolute error, 0.1).
+    So the largest absolute error (0.5, row 0) and the largest relative one
+    (0.125, also row 0) come from the same row here; a second case separates them.
+    """
+    ref = np.array([[1.0, -4.0, 2.0], [0.5, 0.25, -0.5], [0.0, 0.0, 0.0]])
+    got = np.array([[1.5, -4.0, 2.0], [0.5, 0.30, -0.5], [0.0, 0.1, 0.0]])
+    assert oracle.max_abs_err(got, ref) == pytest.approx(0.5, abs=1e-15)
+    assert oracle.max_rownorm_rel_err(got, ref) == pytest.approx(0.125, abs=1e-15)
+    # large absolute error on a large row, small on a small row: the relative
+    # maximum is the small row's (0.01 / 0.02 = 0.5 against 1 / 100 = 0.01)
+    ref2 = np.array([[[100.0, 0.0]], [[0.02, -0.01]]])  # [2, 1, 2]: rows over the last axis
+    got2 = np.array([[[101.0, 0.0]], [[0.02, -0.02]]])
+    assert oracle.max_abs_err(got2, ref2) == pytest.approx(1.0, abs=1e-12)
+    assert oracle.max_rownorm_rel_err(got2, ref2) == pytest.approx(0.5, abs=1e-12)
+    # symmetric in sign, zero for identical inputs, empty input gives 0
+    assert oracle.max_abs_err(-got, -ref) == oracle.max_abs_err(got, ref)
+    assert oracle.max_rownorm_rel_err(ref, ref) == 0.0 and oracle.max_abs_err(ref, ref) == 0.0
+    assert oracle.max_abs_err(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+    assert oracle.max_rownorm_rel_err(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+
+
+def test_comparison_helpers_never_pass_a_nan():
+    """A NaN output makes both errors NaN, which fails every `err <= bar` check."""
+    ref = np.ones((2, 3))
+    got = ref.copy()
+    got[1, 2] = np.nan
+    a, r = oracle.max_abs_err(got, ref), oracle.max_rownorm_rel_err(got, ref)
+    assert math.isnan(a) and math.isnan(r)
+    assert not (a <= 1.0) and not (r <= 1.0)
