@@ -61,6 +61,8 @@ extern "C" {
                                     16-byte aligned */
 #define PKV_ERR_HIP (-6)         /* a kernel launch failed (hipGetLastError after launch) */
 #define PKV_ERR_NO_BLOCKS (-7)   /* block bookkeeping: the free pool is empty */
+#define PKV_ERR_SCRATCH (-8)     /* paged_attn_decode_noalloc: the call needs more partial-state memory than
+                                    the library's buffer holds */
 
 #define PKV_DTYPE_F32 0
 #define PKV_DTYPE_BF16 1
@@ -280,6 +282,28 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
                       float scale, void* out, int32_t partition_tokens, void* workspace,
                       size_t workspace_bytes, void* hip_stream);
+
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same arguments and result as
+ * paged_attn_decode, without the workspace: the partial states of the split
+ * live in a buffer inside the library, paged_attn_decode_noalloc_scratch_bytes()
+ * bytes (16.25 MiB) on each GPU it runs on, held until the process ends and
+ * set up on the first call on that GPU (that GPU must be current).  The call
+ * allocates nothing (no hipMalloc, no allocating library routine).  That
+ * buffer covers the balanced split (partition_tokens == 0) at every supported
+ * shape; fixed partitions whose workspace would exceed it return
+ * PKV_ERR_SCRATCH before anything is launched.  Every call on one GPU shares
+ * that GPU's buffer: two calls that may run at the same time on one GPU (on
+ * different streams without an ordering between them) race and give
+ * undefined results.  Nothing in the buffer needs to start at zero.
+ */
+size_t paged_attn_decode_noalloc_scratch_bytes(void);
+int paged_attn_decode_noalloc(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                              const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                              float scale, void* out, int32_t partition_tokens, void* hip_stream);
 
 /*
  * paged_attn_decode_shared_prefix -- a decode step (as paged_attn_decode) for

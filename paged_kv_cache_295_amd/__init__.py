@@ -19,7 +19,7 @@ __all__ = [
     "paged_attn_decode_shared_prefix", "shared_prefix_workspace_bytes", "paged_kv_copy_blocks", "BlockPool",
     "paged_kv_write_fp8", "paged_attn_decode_fp8", "paged_kv_copy_blocks_fp8",
     "paged_attn_spec_verify", "spec_verify_workspace_bytes", "paged_attn_prefill_chunk_ws",
-    "prefill_chunk_workspace_bytes", "paged_attn_lse_merge",
+    "prefill_chunk_workspace_bytes", "paged_attn_lse_merge", "paged_attn_decode_noalloc", "noalloc_scratch_bytes",
 ]
 
 BLOCK_SIZE = 16
@@ -99,6 +99,10 @@ def load_library():
     lib.paged_attn_spec_verify_workspace_bytes.restype = sz
     lib.paged_attn_spec_verify.argtypes = [vp, i32, i32, i32, vp, vp, vp, cdp, vp, i32, vp, f32, vp, vp, sz, vp]
     lib.paged_attn_spec_verify.restype = ctypes.c_int
+    lib.paged_attn_decode_noalloc.argtypes = [vp, i32, i32, vp, vp, cdp, vp, i32, vp, i32, f32, vp, i32, vp]
+    lib.paged_attn_decode_noalloc.restype = ctypes.c_int
+    lib.paged_attn_decode_noalloc_scratch_bytes.argtypes = []
+    lib.paged_attn_decode_noalloc_scratch_bytes.restype = sz
     lib.paged_attn_lse_merge.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
     lib.paged_attn_lse_merge.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
@@ -296,6 +300,38 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
                                int(max_context_len), float(scale), _ptr(out), int(partition_tokens), ws_ptr,
                                ws_bytes, _stream(stream))
     _check(st, "paged_attn_decode")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the partial-state buffer paged_attn_decode_noalloc keeps on each GPU."""
+    return int(load_library().paged_attn_decode_noalloc_scratch_bytes())
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,
+                              partition_tokens=0, stream=None):
+    """paged_attn_decode without a workspace: the partial states live in the library's own buffer
+    (noalloc_scratch_bytes() per GPU), so the call allocates nothing.  Calls that may overlap on one
+    GPU share that buffer and race."""
+    _on_one_gpu(q, k_cache, v_cache, block_tables, context_lens, out)
+    lib = load_library()
+    _same_dtype(q, out, k_cache, v_cache)
+    desc = _cache_desc(k_cache)
+    B, hq, d = q.shape
+    if out.shape != q.shape or d != desc.head_dim:
+        raise ValueError("q/out must be [B, Hq, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables [B, max_blocks], context_lens [B]")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * BLOCK_SIZE
+    torch = _torch()
+    with torch.cuda.device(q.device):  # the library finds its buffer on the current GPU
+        st = lib.paged_attn_decode_noalloc(_ptr(q), B, hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                                           _i32(block_tables, "block_tables"), max_blocks,
+                                           _i32(context_lens, "context_lens"), int(max_context_len), float(scale),
+                                           _ptr(out), int(partition_tokens), _stream(stream))
+    _check(st, "paged_attn_decode_noalloc")
     return out
 
 

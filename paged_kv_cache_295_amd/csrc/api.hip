@@ -3,6 +3,8 @@
 // caller's stream.  See include/pagedkv.h for the contract of each call.
 #include <math.h>
 
+#include <mutex>
+
 #include "pagedkv.h"
 #include "pkv_internal.hpp"
 
@@ -165,6 +167,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch error";
     case PKV_ERR_NO_BLOCKS: return "no free cache block";
+    case PKV_ERR_SCRATCH: return "the call needs more scratch than the no-allocation decode holds";
   }
   return "unknown status";
 }
@@ -298,6 +301,72 @@ int paged_attn_decode(const void* q, int32_t num_seqs, int32_t num_q_heads, cons
   return decode_common(q, num_seqs, num_q_heads, k_cache, v_cache, nullptr, nullptr, cache, block_tables,
                        max_blocks_per_seq, context_lens, max_context_len, scale, out, partition_tokens, workspace,
                        workspace_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+// ---- decode without allocation ---------------------------------------------
+// The split decode's partial states in a buffer inside the library instead of
+// a caller workspace: enough for the balanced split at every supported shape
+// (the most waves, two partials each, eight heads per wave, head_dim 128), so
+// only fixed partitions of large batches can need more.  Each GPU the library
+// runs on holds its own copy until the process ends.  The kernels write every
+// partial they read later in the same call, so nothing needs clearing.
+static constexpr size_t kScratchBytes = (size_t)balanced_waves_max(8) * 2 * 8 * (128 + 2) * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current GPU's copy of `scratch`, looked up once
+// per device (the array's name in host code is not a device address).
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PKV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attn_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int paged_attn_decode_noalloc(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+                              const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                              float scale, void* out, int32_t partition_tokens, void* hip_stream) {
+  // the checks that size the partial states come first, so an oversized call
+  // fails on the host before anything touches the GPU
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (max_context_len < 0 || partition_tokens < 0 || partition_tokens % PKV_BLOCK_SIZE != 0) return PKV_ERR_SHAPE;
+  const size_t need = partition_tokens == 0
+                          ? balanced_workspace(num_q_heads, cache->num_kv_heads, cache->head_dim)
+                          : partition_workspace(num_seqs, num_q_heads, cache->head_dim, max_context_len,
+                                                partition_tokens);
+  if (need > kScratchBytes) return PKV_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_common(q, num_seqs, num_q_heads, k_cache, v_cache, nullptr, nullptr, cache, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, scale, out, partition_tokens, ws,
+                       need > 0 ? kScratchBytes : 0, hip_stream);
 }
 
 int paged_attn_decode_fp8(const void* q, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,

@@ -43,7 +43,7 @@ def test_abi_version(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, DTYPE, SHAPE, UNSUP, WS, -6, -7):
+    for code in (OK, NULL, DTYPE, SHAPE, UNSUP, WS, -6, -7, -8):
         s = lib.pkv_status_string(code)
         assert s and s != b"unknown status"
     assert lib.pkv_status_string(42) == b"unknown status"
