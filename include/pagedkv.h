@@ -411,12 +411,33 @@ int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, in
                            const int32_t* context_lens, float scale, void* out, void* workspace,
                            size_t workspace_bytes, void* hip_stream);
 
+/*
+ * paged_kv_read_probe -- a measurement aid: reads the K/V bytes a decode call
+ * over the same batch reads, the way its kernel reads them, and computes
+ * nothing else.  ("Part 47", section 5.2: the kernel's cost of following the
+ * block table; the decode step is bound by memory bandwidth.)  Every row
+ * t < context_lens[s] of every (sequence s, kv head) K and V tile reached
+ * through block_tables is loaded with the decode's 16-byte non-temporal
+ * loads, four blocks in flight per wavefront, the batch's blocks divided
+ * evenly over num_waves wavefronts (1 .. 65536); wavefront w folds the 32-bit
+ * words it read with XOR into out_words[w] (device, uint32 [num_waves]), so
+ * no load can be dropped.  Its duration is what the memory system allows for
+ * this access pattern -- a floor under the decode call -- and its hardware
+ * byte counters, against the exact bytes it reads, calibrate those counters
+ * for these loads.  Any cache dtype.  Device-side contract as
+ * paged_attn_decode (a context outside [0, 16 * max_blocks_per_seq] reads
+ * nothing; a block id outside the pool reads block 0).
+ */
+int paged_kv_read_probe(const void* k_cache, const void* v_cache, const pkv_cache_desc* cache,
+                        const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_waves, uint32_t* out_words, void* hip_stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* pkv_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION ((1 << 16) | 6)
+#define PKV_ABI_VERSION ((1 << 16) | 7)
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ __all__ = [
     "paged_kv_write_fp8", "paged_attn_decode_fp8", "paged_kv_copy_blocks_fp8",
     "paged_attn_spec_verify", "spec_verify_workspace_bytes", "paged_attn_prefill_chunk_ws",
     "prefill_chunk_workspace_bytes", "paged_attn_lse_merge", "paged_attn_decode_noalloc", "noalloc_scratch_bytes",
+    "paged_kv_read_probe",
 ]
 
 BLOCK_SIZE = 16
@@ -103,6 +104,8 @@ def load_library():
     lib.paged_attn_decode_noalloc.restype = ctypes.c_int
     lib.paged_attn_decode_noalloc_scratch_bytes.argtypes = []
     lib.paged_attn_decode_noalloc_scratch_bytes.restype = sz
+    lib.paged_kv_read_probe.argtypes = [vp, vp, cdp, vp, i32, i32, vp, i32, vp, vp]
+    lib.paged_kv_read_probe.restype = ctypes.c_int
     lib.paged_attn_lse_merge.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
     lib.paged_attn_lse_merge.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
@@ -544,3 +547,23 @@ def paged_attn_lse_merge(part_o, part_ml, out, stream=None):
     st = lib.paged_attn_lse_merge(_ptr(part_o), _ptr(part_ml), R, P, D, _dtype_code(out), _ptr(out), _stream(stream))
     _check(st, "paged_attn_lse_merge")
     return out
+
+
+def paged_kv_read_probe(k_cache, v_cache, block_tables, context_lens, num_waves, out_words=None, stream=None,
+                        k_scale=None, v_scale=None):
+    """Measurement aid: read the K/V rows a decode over this batch reads, with its loads, over num_waves
+    wavefronts; returns out_words (uint32-valued int32 [num_waves]), wavefront w's XOR of the words it read.
+    fp8 caches pass their scales only to identify the cache (the scales are not read)."""
+    torch = _torch()
+    if out_words is None:
+        out_words = torch.empty(num_waves, dtype=torch.int32, device=k_cache.device)
+    _on_one_gpu(k_cache, v_cache, block_tables, context_lens, out_words)
+    lib = load_library()
+    desc = _fp8_desc(k_cache, v_cache, k_scale, v_scale) if k_scale is not None else _cache_desc(k_cache)
+    if block_tables.dim() != 2 or context_lens.shape != (block_tables.shape[0],) or out_words.shape != (num_waves,):
+        raise ValueError("block_tables [B, max_blocks], context_lens [B], out_words [num_waves]")
+    st = lib.paged_kv_read_probe(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _i32(block_tables, "block_tables"),
+                                 block_tables.shape[0], block_tables.shape[1], _i32(context_lens, "context_lens"),
+                                 int(num_waves), _i32(out_words, "out_words"), _stream(stream))
+    _check(st, "paged_kv_read_probe")
+    return out_words

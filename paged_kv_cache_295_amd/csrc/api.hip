@@ -202,6 +202,21 @@ int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads)
   return balanced_waves(heads_per_wave(num_q_heads / num_kv_heads), PKV_DTYPE_BF16);
 }
 
+int paged_kv_read_probe(const void* k_cache, const void* v_cache, const pkv_cache_desc* cache,
+                        const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_waves, uint32_t* out_words, void* hip_stream) {
+  if (cache == nullptr) return PKV_ERR_NULL;
+  int st = check_cache(cache, cache->dtype == PKV_DTYPE_FP8_E4M3);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_waves <= 0 || num_waves > 65536) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !out_words) return PKV_ERR_NULL;
+  const int elem = cache->dtype == PKV_DTYPE_F32 ? 4 : (cache->dtype == PKV_DTYPE_BF16 ? 2 : 1);
+  return from_hip(launch_read_probe(k_cache, v_cache, block_tables, context_lens, num_seqs, cache->num_kv_heads,
+                                    cache->head_dim, elem, cache->num_blocks, max_blocks_per_seq, num_waves,
+                                    out_words, as_stream(hip_stream)));
+}
+
 int paged_attn_lse_merge(const float* part_o, const float* part_ml, int64_t num_rows, int32_t num_parts,
                          int32_t head_dim, int32_t out_dtype, void* out, void* hip_stream) {
   if (num_rows < 0) return PKV_ERR_SHAPE;

@@ -298,26 +298,31 @@ struct Segment {
   }
 
   // The K and V tiles (16 tokens of one kv head each) of the BPT blocks of a
-  // pipeline tile, block b at byte offset off[b] of the caches.  Every block
-  // is loaded whole (rows past the context in a last block are still inside
-  // it): one constant per-lane offset plus immediates, so no address
-  // arithmetic sits between the loads of consecutive tiles.
+  // pipeline tile, block b at byte offset off[b] of the caches, of which the
+  // first nbytes[b] bytes (whole token rows) are read.  Each block is a
+  // buffer resource of that size over its tile, so rows past the context and
+  // the blocks past a segment's end (size 0) come back as zeros without a
+  // memory access, while the load instructions stay unconditional: one
+  // constant per-lane offset plus immediates, nothing computed per lane
+  // between the loads of consecutive tiles.
   __device__ __forceinline__ void load_tile(Chunk (&kk)[NP][CPL], Chunk (&vv)[NP][CPL], float (&sk)[NSC],
-                                            float (&sv)[NSC], const int64_t (&off)[BPT]) const {
+                                            float (&sv)[NSC], const int64_t (&off)[BPT],
+                                            const int (&nbytes)[BPT]) const {
+    constexpr int kAux = kStreamKV ? 2 : 0;  // cache policy: bit 1 = non-temporal
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int b = 0; b < BPT; ++b) {
+      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + off[b], nbytes[b]);
+      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + off[b], nbytes[b]);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int64_t ob = off[p / PPB];
-        const int o = lane_base + (p % PPB) * TPP * RB + c * LPT * 16;
-        if constexpr (kStreamKV) {
-          kk[p][c] = load_chunk_stream(kc + ob + o);
-          vv[p][c] = load_chunk_stream(vc + ob + o);
-        } else {
-          kk[p][c] = load_chunk(kc + ob + o);
-          vv[p][c] = load_chunk(vc + ob + o);
+      for (int pp = 0; pp < PPB; ++pp)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int p = b * PPB + pp;
+          const int o = lane_base + pp * TPP * RB + c * LPT * 16;
+          kk[p][c] = as_chunk(__builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, kAux));
+          vv[p][c] = as_chunk(__builtin_amdgcn_raw_buffer_load_b128(vr, o, 0, kAux));
         }
-      }
+    }
     if constexpr (kScaled) {
       // a block's 16 scales sit at (block * kv heads + kv head) * 16, i.e. its offset / RB
 #pragma unroll
@@ -387,24 +392,19 @@ struct Segment {
       }
       l[h] = ls;
     }
-    // Rows past `end` may hold NaN: a zero weight is not enough (0 * NaN), so
-    // their V words are replaced by 0.  Selects on every block keep a single
-    // code path.
-    Chunk vz[NP][CPL];
+    // Rows past `end` were not read (the tile's buffer size stops at the
+    // context): their V words are 0 and their weights 0, so they add exactly
+    // nothing.  (Reading them could return the NaN a free slot holds, and
+    // 0 * NaN would poison the sum.)
+    if constexpr (kScaled) {  // the V scale joins the weights (the sums l keep the plain ones)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const bool ok = tok0 + tok_of(p) < end;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) vz[p][c].w[w] = ok ? vv[p][c].w[w] : 0u;
-      if constexpr (kScaled) {  // the V scale joins the weights (the sums l keep the plain ones)
-        const float f = ok ? sv[kScaled ? p : 0] : 0.0f;
+      for (int p = 0; p < NP; ++p) {
+        const float f = tok0 + tok_of(p) < end ? sv[kScaled ? p : 0] : 0.0f;
 #pragma unroll
         for (int h = 0; h < GB; ++h) sc[p][h] *= f;
       }
     }
-    PV<KV, NP, CPL, GB>::apply(sc, vz, acc);
+    PV<KV, NP, CPL, GB>::apply(sc, vv, acc);
   }
 
   // Start from the attention state of a shared prefix: the a.init_splits
@@ -484,46 +484,66 @@ struct Segment {
       return (int64_t)p * blk_stride + (int64_t)g * kTileBytes;
     };
     auto block_off = [&](int jb) -> int64_t { return tile_off(table[jb]); };
+    // bytes of segment block jb that hold tokens before `end` (0 past the segment)
+    auto block_bytes = [&](int jb) -> int {
+      const int v = end - (blk0 + jb) * kBlock;
+      return v <= 0 ? 0 : (v >= kBlock ? kBlock * RB : v * RB);
+    };
 
     // NS register stages of BPT blocks each: while tile jt is computed, tiles
     // jt+1 .. jt+NS-1 are in flight and tile jt+NS is issued right after.  The
     // prologue fills every stage so that the loop is entered in its steady
-    // state; past the end loads re-read the last block (an L2 hit), so no load
-    // is conditional.  The body computes NS tiles and exits only at its end (a
-    // single exit keeps the accumulators in place); blocks past the last one
-    // lie wholly past `end`, are masked and add exactly nothing.  Table entries
-    // are fetched one pass ahead.
+    // state; past the end the loads have a buffer size of 0 (no memory access,
+    // zeros), so no load is conditional.  The body computes NS tiles and exits
+    // only at its end (a single exit keeps the accumulators in place); blocks
+    // past the last one lie wholly past `end`, are masked and add exactly
+    // nothing.  Table entries are fetched one pass ahead.
     constexpr int TB = NS * BPT;  // blocks per loop pass
     Chunk kS[NS][NP][CPL], vS[NS][NP][CPL];
     float skS[NS][NSC], svS[NS][NSC];
     const int last = nblk - 1;
     int64_t offs[NS][BPT];
+    int nbs[NS][BPT];
     int first[2 * TB];  // the first 2 NS tiles' entries, fetched together
 #pragma unroll
     for (int i = 0; i < 2 * TB; ++i) first[i] = table[min(i, last)];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       int64_t o[BPT];
+      int nb[BPT];
 #pragma unroll
-      for (int b = 0; b < BPT; ++b) o[b] = tile_off(first[st * BPT + b]);
-      load_tile(kS[st], vS[st], skS[st], svS[st], o);
+      for (int b = 0; b < BPT; ++b) {
+        o[b] = tile_off(first[st * BPT + b]);
+        nb[b] = block_bytes(st * BPT + b);
+      }
+      load_tile(kS[st], vS[st], skS[st], svS[st], o, nb);
       // each stage's loads are issued before the next stage's: waits are in order
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
 #pragma unroll
-      for (int b = 0; b < BPT; ++b) offs[st][b] = tile_off(first[TB + st * BPT + b]);
+      for (int b = 0; b < BPT; ++b) {
+        offs[st][b] = tile_off(first[TB + st * BPT + b]);
+        nbs[st][b] = block_bytes(TB + st * BPT + b);
+      }
     for (int jb = 0;; jb += TB) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         compute(kS[st], vS[st], skS[st], svS[st], (blk0 + jb + st * BPT) * kBlock + tg, end);
         int64_t next[BPT];
+        int nextb[BPT];
 #pragma unroll
-        for (int b = 0; b < BPT; ++b) next[b] = block_off(min(jb + 2 * TB + st * BPT + b, last));
-        load_tile(kS[st], vS[st], skS[st], svS[st], offs[st]);
+        for (int b = 0; b < BPT; ++b) {
+          next[b] = block_off(min(jb + 2 * TB + st * BPT + b, last));
+          nextb[b] = block_bytes(jb + 2 * TB + st * BPT + b);
+        }
+        load_tile(kS[st], vS[st], skS[st], svS[st], offs[st], nbs[st]);
 #pragma unroll
-        for (int b = 0; b < BPT; ++b) offs[st][b] = next[b];
+        for (int b = 0; b < BPT; ++b) {
+          offs[st][b] = next[b];
+          nbs[st][b] = nextb[b];
+        }
       }
       if (jb + TB >= nblk) break;
     }
@@ -795,6 +815,19 @@ __device__ __forceinline__ void cost_counts(const int32_t* __restrict__ lens, in
   before = uniform64(before);
 }
 
+// Total blocks of all sequences times HH (every lane gets it).
+__device__ __forceinline__ void cost_counts_blocks(const int32_t* __restrict__ lens, int B, int cap, int HH,
+                                                   int64_t& total, int64_t& unused) {
+  total = 0;
+  unused = 0;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int i = c0 + __lane_id();
+    const int64_t incl = wave_incl_scan(i < B ? (int64_t)seq_blocks(lens[i], cap) * HH : 0);
+    total += readlane64(incl, kWave - 1);
+  }
+  total = uniform64(total);
+}
+
 __device__ __forceinline__ int64_t range_begin(int w, int W, int64_t U) { return (int64_t)w * U / W; }
 // The wave whose range holds cost unit u.
 __device__ __forceinline__ int wave_of(int64_t u, int W, int64_t U) { return (int)(((u + 1) * W + U - 1) / U) - 1; }
@@ -1049,6 +1082,135 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
 #pragma unroll
     for (int e = 0; e < PER; ++e) outp[h * D + lane + e * kWave] = (T)(o[h][e] * inv);
   }
+}
+
+// ---------------------------------------------------------------- read probe
+//
+// The bytes a decode call's K/V loads touch, read the way it reads them and
+// nothing else: every (sequence, kv head) tile row before the context length,
+// 16-byte non-temporal buffer loads sized to the valid rows, four blocks in
+// flight per wave, the batch's blocks (in sequence, kv head, block order)
+// divided evenly over the grid.  Each wave folds what it read into one word
+// (XOR) so that no load can be dropped.  No attention: the duration is what
+// the memory system allows for this access pattern.
+template <int RB>
+__global__ __launch_bounds__(64) void read_probe_kernel(const char* __restrict__ kc, const char* __restrict__ vc,
+                                                        const int32_t* __restrict__ tables,
+                                                        const int32_t* __restrict__ lens, int B, int Hkv,
+                                                        int num_blocks, int max_blocks, uint32_t* __restrict__ out) {
+  constexpr int kTile = kBlock * RB;
+  constexpr int kLoads = kTile / (kWave * 16);  // 16-byte loads per lane per tile
+  static_assert(kLoads >= 1 && kTile % (kWave * 16) == 0, "a tile is whole 1 KiB rows of the wave");
+  constexpr int NS = 4;
+  const int lane = __lane_id();
+  const int W = gridDim.x, w = blockIdx.x;
+  const int cap = max_blocks * kBlock;
+  int64_t T, unused;
+  cost_counts_blocks(lens, B, cap, Hkv, T, unused);
+  const int64_t b0 = (int64_t)w * T / W, b1 = (int64_t)(w + 1) * T / W;
+  uint32_t acc = 0;
+  if (b0 < b1) {
+    // locate b0: sequence s, kv head g, block j
+    int s = 0;
+    int64_t cum = 0;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const int i = c0 + lane;
+      const int64_t c = i < B ? (int64_t)seq_blocks(lens[i], cap) * Hkv : 0;
+      const int64_t incl = wave_incl_scan(c);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && cum + incl > b0);
+      if (hit) {
+        const int ln = __builtin_ctzll(hit);
+        s = c0 + ln;
+        cum += readlane64(incl - c, ln);
+        break;
+      }
+      cum += readlane64(incl, kWave - 1);
+    }
+    s = __builtin_amdgcn_readfirstlane(s);
+    cum = uniform64(cum);
+    int L = lens[s];
+    int nb = seq_blocks(L, cap);
+    int g = (int)((b0 - cum) / nb);
+    int j = (int)(b0 - cum - (int64_t)g * nb);
+    const int64_t head_stride = kTile, blk_stride = (int64_t)kTile * Hkv;
+    // the tile of the next block to load, advancing (s, g, j); past b1 a size of 0
+    int64_t left = b1 - b0;
+    auto next_tile = [&](int64_t& off, int& bytes) {
+      if (left <= 0) {
+        off = 0;
+        bytes = 0;
+        return;
+      }
+      --left;
+      int p = tables[(int64_t)s * max_blocks + j];
+      p = (p < 0 || p >= num_blocks) ? 0 : p;
+      off = (int64_t)p * blk_stride + (int64_t)g * head_stride;
+      const int v = L - j * kBlock;
+      bytes = (v >= kBlock ? kBlock : v) * RB;
+      if (++j == nb) {
+        j = 0;
+        if (++g == Hkv) {
+          g = 0;
+          do {  // the next sequence with blocks (one exists while left > 0)
+            ++s;
+            L = s < B ? lens[s] : 0;
+            nb = s < B ? seq_blocks(L, cap) : 1;
+          } while (nb == 0 && s < B);
+        }
+      }
+    };
+    Chunk kS[NS][kLoads], vS[NS][kLoads];
+    auto issue = [&](Chunk (&kk)[kLoads], Chunk (&vv)[kLoads]) {
+      int64_t off;
+      int bytes;
+      next_tile(off, bytes);
+      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + off, bytes), vr = tile_rsrc(vc + off, bytes);
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        kk[i] = as_chunk(__builtin_amdgcn_raw_buffer_load_b128(kr, (i * kWave + lane) * 16, 0, 2));
+        vv[i] = as_chunk(__builtin_amdgcn_raw_buffer_load_b128(vr, (i * kWave + lane) * 16, 0, 2));
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < NS; ++st) issue(kS[st], vS[st]);
+    for (int64_t n = b1 - b0; n > 0; n -= NS) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc ^= kS[st][i].w[e] ^ vS[st][i].w[e];
+        issue(kS[st], vS[st]);
+      }
+    }
+  }
+  // one word per wave: the XOR over its lanes
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) acc ^= (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, (int)acc);
+  if (lane == 0) out[w] = acc;
+}
+
+hipError_t launch_read_probe(const void* k_cache, const void* v_cache, const int32_t* tables, const int32_t* lens,
+                             int num_seqs, int num_kv_heads, int head_dim, int elem_bytes, int num_blocks,
+                             int max_blocks, int waves, uint32_t* out, hipStream_t stream) {
+  const char* kc = reinterpret_cast<const char*>(k_cache);
+  const char* vc = reinterpret_cast<const char*>(v_cache);
+  const int rb = head_dim * elem_bytes;
+  if (rb == 256)
+    hipLaunchKernelGGL(read_probe_kernel<256>, dim3(waves), dim3(64), 0, stream, kc, vc, tables, lens, num_seqs,
+                       num_kv_heads, num_blocks, max_blocks, out);
+  else if (rb == 128)
+    hipLaunchKernelGGL(read_probe_kernel<128>, dim3(waves), dim3(64), 0, stream, kc, vc, tables, lens, num_seqs,
+                       num_kv_heads, num_blocks, max_blocks, out);
+  else if (rb == 512)
+    hipLaunchKernelGGL(read_probe_kernel<512>, dim3(waves), dim3(64), 0, stream, kc, vc, tables, lens, num_seqs,
+                       num_kv_heads, num_blocks, max_blocks, out);
+  else if (rb == 64)
+    hipLaunchKernelGGL(read_probe_kernel<64>, dim3(waves), dim3(64), 0, stream, kc, vc, tables, lens, num_seqs,
+                       num_kv_heads, num_blocks, max_blocks, out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // Shared prefix: merge the `splits` partials of every (sequence, head) row

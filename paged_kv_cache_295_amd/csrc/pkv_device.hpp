@@ -40,6 +40,23 @@ __device__ __forceinline__ Chunk load_chunk_stream(const void* p) {
   return c;
 }
 
+// A raw buffer resource over the `bytes` bytes at p (stride 0; the fourth
+// descriptor word is the gfx9 one for untyped 32-bit data).  A load whose
+// 16 bytes do not lie wholly inside [0, bytes) returns zeros and makes no
+// memory access, so a size that stops at the last valid row masks the rest
+// of a tile for free, and size 0 turns a load into a no-op.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Chunk as_chunk(i32x4_t v) {
+  Chunk c;
+  c.w[0] = (uint32_t)v.x; c.w[1] = (uint32_t)v.y; c.w[2] = (uint32_t)v.z; c.w[3] = (uint32_t)v.w;
+  return c;
+}
+
 __device__ __forceinline__ void store_chunk(void* p, const Chunk& c) {
   *reinterpret_cast<uint4*>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
 }

@@ -105,6 +105,10 @@ hipError_t launch_prefix_mfma(const PrefillArgs& a, hipStream_t stream);
 // out [rows][head_dim] of out_dtype (0 float32, 1 bfloat16).
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int64_t rows, int parts, int head_dim,
                             int out_dtype, void* out, hipStream_t stream);
+// The read probe: the K/V bytes of a decode call, read with its loads over `waves` waves.
+hipError_t launch_read_probe(const void* k_cache, const void* v_cache, const int32_t* tables, const int32_t* lens,
+                             int num_seqs, int num_kv_heads, int head_dim, int elem_bytes, int num_blocks,
+                             int max_blocks, int waves, uint32_t* out, hipStream_t stream);
 // Merges the splits partials of each of `rows` rows into the first split's slot.
 hipError_t launch_prefix_merge(float* part_o, float* part_ml, int64_t rows, int splits, int head_dim,
                                hipStream_t stream);

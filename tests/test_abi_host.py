@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == (1 << 16) | 6
+    assert lib.pkv_abi_version() == (1 << 16) | 7
 
 
 def test_status_strings(lib):
@@ -302,3 +302,14 @@ def test_binding_rejects_host_tensors_before_any_call(monkeypatch):
         pkv.paged_kv_write_fp8(q[:, :8], q[:, :8], lens, u8, u8, sc, sc)
     with pytest.raises(ValueError, match="on the GPU"):
         pkv.paged_kv_copy_blocks_fp8(lens, lens, u8, u8, sc, sc)
+
+
+def test_read_probe_validation(lib):
+    p = lib.paged_kv_read_probe
+    d = desc()
+    assert p(FAKE, FAKE, None, FAKE, 2, 4, FAKE, 8, FAKE, None) == NULL
+    assert p(FAKE, FAKE, ctypes.byref(d), FAKE, -1, 4, FAKE, 8, FAKE, None) == SHAPE
+    assert p(FAKE, FAKE, ctypes.byref(d), FAKE, 2, 4, FAKE, 0, FAKE, None) == SHAPE
+    assert p(FAKE, FAKE, ctypes.byref(d), FAKE, 2, 4, FAKE, 1 << 17, FAKE, None) == SHAPE
+    assert p(FAKE, FAKE, ctypes.byref(d), FAKE, 2, 4, FAKE, 8, None, None) == NULL
+    assert p(FAKE, FAKE, ctypes.byref(desc(d=96)), FAKE, 2, 4, FAKE, 8, FAKE, None) == UNSUP
