@@ -307,12 +307,17 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     qrow = reinterpret_cast<const __bf16*>(a.q) + (out_row * a.num_q_heads + head) * D;
   }
 
+  // The softmax works on raw scores and folds the scale into the exponent's
+  // FMA, which needs a positive scale: a negative one flips the sign of q
+  // (exact in bf16) and of the scale.
+  const float sl2 = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
   bf16x8_t qop[S::kKSteps];
 #pragma unroll
   for (int kk = 0; kk < S::kKSteps; ++kk) {
     if (row_ok) {
       const Chunk ch = load_chunk(qrow + kk * 16 + 8 * half);
-      qop[kk] = as_bf16x8(ch.w[0], ch.w[1], ch.w[2], ch.w[3]);
+      qop[kk] = as_bf16x8(ch.w[0] ^ qsign, ch.w[1] ^ qsign, ch.w[2] ^ qsign, ch.w[3] ^ qsign);
     } else {
       qop[kk] = as_bf16x8(0u, 0u, 0u, 0u);
     }
@@ -410,7 +415,6 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   for (int nd = 0; nd < S::kND; ++nd)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[nd][v] = 0.0f;
-  const float sl2 = a.scale_log2;
 
   // a wave whose 32 rows carry no query only loads and synchronises
   const bool wave_active = __builtin_amdgcn_ballot_w64(row_ok) != 0;
@@ -439,21 +443,21 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   // position (diagonal tiles).
   auto finish = [&](auto mask_tag, int kt, f32x16_t (&st)[kNB], int vbase) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    // scale, causal mask (select, diagonal tiles only), row max over this lane and lane ^ 32
+    // causal mask (select, diagonal tiles only) and the row max of the raw
+    // scores over this lane and lane ^ 32; the scale (positive) is applied to
+    // the max once and to each score inside the exponent's FMA
+    // (masked keys are left out of the max and get weight 0 by a select on the
+    // weight, so neither their K rows -- possibly NaN -- nor a zero scale can
+    // leak into the sums)
+    auto masked = [&](int nb, int v) {
+      return kt * kKT + nb * 32 + 8 * (v >> 2) + 4 * half + (v & 3) > qpos;
+    };
     float mx = -__builtin_inff();
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = st[nb][v] * sl2;
-        if constexpr (MASK) {
-          const int kpos = kt * kKT + nb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          x = kpos > qpos ? -__builtin_inff() : x;
-        }
-        st[nb][v] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, (MASK && masked(nb, v)) ? -__builtin_inff() : st[nb][v]);
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * sl2;
     // Lazy rescale: the running max moves (and O, l are rescaled) only when a
     // score exceeds it by more than 2^8, which bounds every P by 256; the
     // final normalisation makes the stale max exact.
@@ -469,16 +473,23 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     }
     const float mn = m_run;
 
+    // P in bf16 for the matrix cores; the running sum adds those same rounded
+    // weights, two at a time (v_dot2 with (1, 1)), so O and l share their weights
     uint32_t pk[kNB][8];
     float ps = 0.0f;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float p0 = fast_exp2(st[nb][2 * u] - mn);
-        const float p1 = fast_exp2(st[nb][2 * u + 1] - mn);
-        ps += p0 + p1;
+        float p0 = fast_exp2(fmaf(st[nb][2 * u], sl2, -mn));
+        float p1 = fast_exp2(fmaf(st[nb][2 * u + 1], sl2, -mn));
+        if constexpr (MASK) {
+          p0 = masked(nb, 2 * u) ? 0.0f : p0;
+          p1 = masked(nb, 2 * u + 1) ? 0.0f : p1;
+        }
         pk[nb][u] = pack_bf16x2(p0, p1);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[nb][u]), ones, ps, false);
       }
     l_run += ps;
 
@@ -637,11 +648,11 @@ static hipError_t launch_chunk_modes(const PrefillArgs& a, int64_t grid, hipStre
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   if (G < 1 || G > kMRows) return hipErrorInvalidValue;
-  const int QT = tile_rows(a.chunk_len_max, G);
-  const int64_t n_mt = (a.chunk_len_max + QT - 1) / QT;
   const bool split = a.num_splits > 1;
   if (split && (a.split_tokens <= 0 || a.split_tokens % kKT != 0 || !a.part_o || !a.part_ml))
     return hipErrorInvalidValue;
+  const int QT = tile_rows(a.chunk_len_max, G);
+  const int64_t n_mt = (a.chunk_len_max + QT - 1) / QT;
   const int64_t grid = n_mt * a.num_chunks * a.num_kv_heads * (split ? a.num_splits : 1);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;

@@ -773,3 +773,27 @@ def test_block_pool_serving_run_on_device():
             assert bits(kc).tobytes() == kc_h.tobytes() and bits(vc).tobytes() == vc_h.tobytes()
             check_attn(values(out), oracle.decode(q, kc_h, vc_h, tab, ln, scale, "bf16"), "bf16", f"step {step}")
     assert n_copies >= 4
+
+
+def test_prefill_score_far_above_the_first_tile():
+    """A key whose score rises far above every score of the chunk's first key tile
+    (about 2^160 in weight): the matrix-core kernel's online softmax moves its
+    reference max and rescales what it accumulated, and the result is still the
+    oracle's (rows before that key unaffected, rows after it dominated by it)."""
+    w = chunk_workload("bf16", 32, 8, 128, [(0, 200), (100, 150)], seed=23)
+    ones = workloads.f32_to_bf16_bits(np.ones(128, np.float32))
+    big = workloads.f32_to_bf16_bits(np.full(128, 10.0, np.float32))
+    for c in range(w.num_chunks):
+        n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+        w.q_chunk[c, :n] = ones  # every valid row: all ones
+    slot_row = {int(sl): i for i, sl in enumerate(w.slot_mapping.tolist())}
+    for c in range(w.num_chunks):
+        for pos in (70, 130):  # keys in the second and third 64-key tiles
+            if pos >= int(w.chunk_context_lens[c]):
+                continue
+            slot = int(w.chunk_tables[c, pos // 16]) * 16 + pos % 16
+            if slot in slot_row:  # written by this step
+                w.new_k[slot_row[slot]] = big
+            else:  # already in the cache
+                w.k_cache[slot // 16, :, slot % 16, :] = big
+    write_decode_prefill_vs_oracle(w, "prefill, a score far above the first tile")
