@@ -42,15 +42,17 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 # HBM traffic of one decode call, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch summed over the call's two
-# kernels), scaled by what the same counters read for a device copy of 256 MiB
-# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by (workload, --kv-dtype).  Valid
-# only for the decode kernel sources it was measured on: reported as null once
-# their hash differs.
+# kernels), scaled by what the same counters read for kernels of known bytes in
+# the same runs: the read probe, which reads exactly the call's K/V rows with the
+# decode's own 16-byte non-temporal buffer loads (FETCH_SIZE x 1.998), and a
+# 256 MiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); factors 2.0 and 1.0
+# are used.  Keyed by (workload, --kv-dtype).  Valid only for the decode kernel
+# sources it was measured on: reported as null once their hash differs.
 TRAFFIC = {
-    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 530040320, "write_bytes": 3422147,
-                                        "sources_sha256": "2262b5bf93b717dec9a5f08df814efd21811532944d60e19fcd16b1bde5ecf7d"},
-    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 284962795, "write_bytes": 5462576,
-                                      "sources_sha256": "2262b5bf93b717dec9a5f08df814efd21811532944d60e19fcd16b1bde5ecf7d"},
+    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 510061773, "write_bytes": 3421696,
+                                        "sources_sha256": "527cb7e9bdb994ed40f0e3645d0b3a7ac90ecf8732a24f17b3e64bd322d9f7d3"},
+    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 277115085, "write_bytes": 5462528,
+                                      "sources_sha256": "527cb7e9bdb994ed40f0e3645d0b3a7ac90ecf8732a24f17b3e64bd322d9f7d3"},
 }
 CSRC = os.path.join(ROOT, "paged_kv_cache_295_amd", "csrc")
 DECODE_SOURCES = ("decode.hip", "pkv_device.hpp", "pkv_internal.hpp")

@@ -424,9 +424,11 @@ int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, in
  * no load can be dropped.  Its duration is what the memory system allows for
  * this access pattern -- a floor under the decode call -- and its hardware
  * byte counters, against the exact bytes it reads, calibrate those counters
- * for these loads.  Any cache dtype.  Device-side contract as
- * paged_attn_decode (a context outside [0, 16 * max_blocks_per_seq] reads
- * nothing; a block id outside the pool reads block 0).
+ * for these loads.  Any cache dtype; of an E4M3 cache it reads the codes
+ * only (the per-row scales a decode also reads are left out).  Device-side
+ * contract as paged_attn_decode (a context outside
+ * [0, 16 * max_blocks_per_seq] reads nothing; a block id outside the pool
+ * reads block 0).
  */
 int paged_kv_read_probe(const void* k_cache, const void* v_cache, const pkv_cache_desc* cache,
                         const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
