@@ -549,10 +549,58 @@ struct Segment {
     }
   }
 
-  // Combine the 64 / LPT token-group streams (every lane ends with the totals):
-  // agree on the largest running max, rescale to it, then add.
+  // The token groups' outputs are combined by a reduce-scatter: each halving
+  // step across one lane bit that separates the groups (permlane32 / permlane16
+  // swaps, a row rotate by 8) adds the partner's half of the values this lane
+  // keeps and drops the other half, so that after the last step the lanes of
+  // group tg hold the totals of flat values [tg * kR, (tg + 1) * kR) of the
+  // [GB][CPL][EPC] output (head-major), and every group stores one piece.
+  // Against an all-reduce of all GB * CPL * EPC values this moves and adds
+  // kN (1/2 + 1/4 + 1/8) values instead of 3 kN.
+  static constexpr int kGroups = kWave / LPT;
+  static constexpr int kN = GB * CPL * EPC;
+  static constexpr int kR = kN / kGroups;                     // values a lane keeps
+  static constexpr int kRun = kR < EPC ? kR : EPC;            // contiguous dims of one store
+  static constexpr bool kScatter = (LPT == 8 || LPT == 16) && kN % kGroups == 0 &&
+                                   (kR <= EPC ? EPC % kR == 0 : kR % EPC == 0) && kRun % 4 == 0 &&
+                                   (kRun * (int)sizeof(T)) % 16 == 0;
+
+  // Flat value v of the [GB][CPL][EPC] outputs (v a constant once the loops
+  // around a call are unrolled, so the array stays in registers).
+  __device__ __forceinline__ float& at(int v) { return acc[v / (CPL * EPC)][(v / EPC) % CPL][v % EPC]; }
+  __device__ __forceinline__ float at(int v) const { return acc[v / (CPL * EPC)][(v / EPC) % CPL][v % EPC]; }
+
+  // Flat values [0, N) -> [0, N / 2): lanes whose bit 5 (k32) or bit 4 is
+  // clear keep the totals of the first half, the others those of the second.
+  template <int N, bool k32>
+  __device__ __forceinline__ void halve_swap() {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const uint32_t a = __builtin_bit_cast(uint32_t, at(i)), b = __builtin_bit_cast(uint32_t, at(i + N / 2));
+      const auto r = k32 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                         : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+      at(i) = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+    }
+  }
+  // The same across lane bit 3 (lanes l and l ^ 8 of a row of 16: rotate by 8).
+  template <int N>
+  __device__ __forceinline__ void halve_ror8() {
+    const bool upper = (__lane_id() & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float send = upper ? at(i) : at(i + N / 2);
+      const float mine = upper ? at(i + N / 2) : at(i);
+      at(i) = mine + dpp_f32<0x128>(send);
+    }
+  }
+
+  // Combine the 64 / LPT token-group streams: agree on the largest running
+  // max and rescale to it; m and l are summed into every lane, the outputs too
+  // where the reduce-scatter does not apply (else the store that follows
+  // scatters them).
   __device__ __forceinline__ void merge_groups() {
     static_assert(LPT == 4 || LPT == 8 || LPT == 16, "token groups differ in lane bits 2..5, 3..5 or 4..5");
+    bad_block = __builtin_amdgcn_ballot_w64(bad_block) != 0;
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
       const float M = groups_max<LPT>(m[h]);
@@ -562,13 +610,55 @@ struct Segment {
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][c][e] = groups_add<LPT>(acc[h][c][e] * f);
+        for (int e = 0; e < EPC; ++e) acc[h][c][e] = kScatter ? acc[h][c][e] * f : groups_add<LPT>(acc[h][c][e] * f);
     }
   }
 
+  // The reduce-scatter itself (the stores call it once, after merge_groups).
+  __device__ __forceinline__ void scatter() {
+    halve_swap<kN, true>();
+    halve_swap<kN / 2, false>();
+    if constexpr (LPT == 8) halve_ror8<kN / 4>();
+  }
+
+  // Which of the GB heads flat value tg * kR + r (this lane's kept range)
+  // belongs to, and the output offset of its dims: head * D + (c * LPT + li) *
+  // EPC + e.
+  __device__ __forceinline__ int kept_offset(int r, int& head) const {
+    const int v = tg * kR + r;
+    head = v / (CPL * EPC);
+    const int c = (v / EPC) % CPL, e = v % EPC;
+    return head * D + (c * LPT + li) * EPC + e;
+  }
   // Normalised output of the GB heads at outp (head h0 of the row).
-  __device__ __forceinline__ void store_out(T* __restrict__ outp) const {
+  __device__ __forceinline__ void store_out(T* __restrict__ outp) {
     const float nan = __builtin_nanf("");
+    if constexpr (kScatter) {
+      // normalise per head first (every head's sum is in every lane), then scatter
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const float inv = bad_block ? nan : 1.0f / l[h];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[h][c][e] *= inv;
+      }
+      scatter();
+      constexpr int QE = 16 / (int)sizeof(T);  // output elements per 16-byte store
+#pragma unroll
+      for (int r = 0; r < kR; r += kRun) {
+        int head;
+        const int off = kept_offset(r, head);
+#pragma unroll
+        for (int j = 0; j < kRun; j += QE) {
+          float o[QE];
+#pragma unroll
+          for (int e = 0; e < QE; ++e) o[e] = at(r + j + e);
+          store_chunk(outp + off + j, Elem<T>::narrow(o));
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
       if (tg != h % TPP) continue;
@@ -589,23 +679,43 @@ struct Segment {
   // Partial (m, l, unnormalised o) of head h at po + h * ostride (D floats) and
   // pml + h * mlstride (2 floats).
   __device__ __forceinline__ void store_partial(float* __restrict__ po, int64_t ostride, float* __restrict__ pml,
-                                                int64_t mlstride) const {
+                                                int64_t mlstride) {
     const float nan = __builtin_nanf("");
+    if constexpr (kScatter) {
+      scatter();
+#pragma unroll
+      for (int r = 0; r < kR; r += kRun) {
+        int head;
+        const int off = kept_offset(r, head);
+        float* o = po + head * ostride + (off - head * D);
+#pragma unroll
+        for (int j = 0; j < kRun; j += 4) {
+          float4 v4;
+          v4.x = at(r + j);
+          v4.y = at(r + j + 1);
+          v4.z = at(r + j + 2);
+          v4.w = at(r + j + 3);
+          *reinterpret_cast<float4*>(o + j) = v4;
+        }
+      }
+    }
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
       if (tg != h % TPP) continue;
-      float* o = po + h * ostride;
+      if constexpr (!kScatter) {
+        float* o = po + h * ostride;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
+        for (int c = 0; c < CPL; ++c)
 #pragma unroll
-        for (int e4 = 0; e4 < EPC; e4 += 4) {
-          float4 v4;
-          v4.x = acc[h][c][e4];
-          v4.y = acc[h][c][e4 + 1];
-          v4.z = acc[h][c][e4 + 2];
-          v4.w = acc[h][c][e4 + 3];
-          *reinterpret_cast<float4*>(o + (c * LPT + li) * EPC + e4) = v4;
-        }
+          for (int e4 = 0; e4 < EPC; e4 += 4) {
+            float4 v4;
+            v4.x = acc[h][c][e4];
+            v4.y = acc[h][c][e4 + 1];
+            v4.z = acc[h][c][e4 + 2];
+            v4.w = acc[h][c][e4 + 3];
+            *reinterpret_cast<float4*>(o + (c * LPT + li) * EPC + e4) = v4;
+          }
+      }
       if (li == 0) {
         pml[h * mlstride] = bad_block ? nan : m[h];
         pml[h * mlstride + 1] = l[h];
