@@ -231,6 +231,15 @@ __device__ __forceinline__ void group_sum_all(float (&x)[N]) {
 // after the final normalisation.
 constexpr float kRescaleSlack = 8.0f;
 
+// bf16 caches take the matrix-core scores only with a deep register
+// pipeline: its longer chain per block (products, a lane exchange, the
+// softmax, ds_bpermute) is hidden by four blocks in flight but not by two (the
+// shared-prefix suffixes, two stages: 98.9 us per call with it, 94.3 without;
+// the Llama-3-8B batch, four stages: 93.1 against 94.7 us).
+#ifndef PKV_DECODE_MFMA_BF16_MIN_STAGES
+#define PKV_DECODE_MFMA_BF16_MIN_STAGES 3
+#endif
+
 // One wave's attention state for GB query heads of one kv head over a run of
 // consecutive blocks of one sequence (a "segment"): the query chunks, and per
 // token group the running max m (log2 units), sum l and unnormalised output.
@@ -248,7 +257,26 @@ struct Segment {
   // scales carried per stage (one dummy entry when there are none)
   static constexpr int NSC = kScaled ? NP : 1;
 
+  // Scores on the matrix cores (bf16 and E4M3 caches, D = 128, four query
+  // heads per wave): the scores of a block's 16 tokens are one chain of
+  // v_mfma_f32_16x16x32_bf16 over the head dims, heads as the rows (4 of the
+  // 16 used) and tokens as the columns, so no lane computes a partial dot
+  // product and no score is reduced across lanes.  Lane l = 16 q + n holds K
+  // bytes [64 j + 16 q, 64 j + 16 q + 16) of token n of the block (chunk j; the
+  // B operand of the products over those dims), and Q the same dims of head n
+  // (the A operand; zero rows for n >= 4).  The scores land in lanes n < 16,
+  // four heads each; there the softmax runs once per (token, head) with the
+  // running max shared by tokens n and n + 8 (the two tokens a value lane
+  // holds), and ds_bpermute hands each value lane its two tokens' weights.
+  static constexpr bool kMfmaK =
+      (std::is_same<KV, Fp8E4M3>::value || (std::is_same<KV, __bf16>::value && NS >= PKV_DECODE_MFMA_BF16_MIN_STAGES)) &&
+      D == 128 && GB == 4 && LPT == 8;
+  static constexpr int kKC = RB / 64;  // K chunks per lane per block
+  static_assert(!kMfmaK || (BPT == 1 && NP * CPL == kKC && NP == 2 && TPP == 8), "one block per tile");
+
   Chunk qv[GB][CPL][QPC];
+  bf16x8_t qa[4];        // matrix-core path: Q as the A operand of the four products
+  float mm[GB], ml[GB];  // matrix-core path: running max / sum of token n's group, lanes n < 16
   float m[GB], l[GB], acc[GB][CPL][EPC];
   bool bad_block;
   int tg, li;
@@ -275,6 +303,18 @@ struct Segment {
 
   // The chunks of the GB query rows at qrow (head h0 of the row) this lane multiplies.
   __device__ __forceinline__ void load_q(const T* __restrict__ qrow) {
+    if constexpr (kMfmaK) {
+      const int lane = __lane_id();
+      const int hm = lane & 15, q = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // the dims product i takes from lane group q (bf16: chunk i; E4M3: half i % 2 of chunk i / 2)
+        const int dim = std::is_same<KV, __bf16>::value ? 32 * i + 8 * q : 64 * (i >> 1) + 16 * q + 8 * (i & 1);
+        const Chunk c = hm < GB ? load_chunk(qrow + hm * D + dim) : Chunk{};
+        qa[i] = as_bf16x8(c.w[0], c.w[1], c.w[2], c.w[3]);
+      }
+      return;
+    }
     constexpr int QE = 16 / (int)sizeof(T);  // query elements per chunk
 #pragma unroll
     for (int h = 0; h < GB; ++h)
@@ -289,6 +329,8 @@ struct Segment {
     for (int h = 0; h < GB; ++h) {
       m[h] = kMaxInit;
       l[h] = 0.0f;
+      mm[h] = kMaxInit;
+      ml[h] = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -309,6 +351,27 @@ struct Segment {
                                             float (&sv)[NSC], const int64_t (&off)[BPT],
                                             const int (&nbytes)[BPT]) const {
     constexpr int kAux = kStreamKV ? 2 : 0;  // cache policy: bit 1 = non-temporal
+    if constexpr (kMfmaK) {
+      const int lane = __lane_id();
+      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + off[0], nbytes[0]);
+      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + off[0], nbytes[0]);
+      const int kbase = (lane & 15) * RB + 16 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < kKC; ++j)
+        kk[j / CPL][j % CPL] = as_chunk(__builtin_amdgcn_raw_buffer_load_b128(kr, kbase + 64 * j, 0, kAux));
+#pragma unroll
+      for (int pp = 0; pp < PPB; ++pp)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          vv[pp][c] = as_chunk(
+              __builtin_amdgcn_raw_buffer_load_b128(vr, lane_base + pp * TPP * RB + c * LPT * 16, 0, kAux));
+      if constexpr (kScaled) {  // the scales of token n = lane % 16
+        const int64_t so = off[0] / RB + (lane & 15);
+        sk[0] = __builtin_nontemporal_load(ksc + so);
+        sv[0] = __builtin_nontemporal_load(vsc + so);
+      }
+      return;
+    }
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
       const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + off[b], nbytes[b]);
@@ -340,6 +403,10 @@ struct Segment {
   // paths cost the register pipeline its fixed placement.)
   __device__ __forceinline__ void compute(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
                                           const float (&sk)[NSC], const float (&sv)[NSC], int tok0, int end) {
+    if constexpr (kMfmaK) {
+      compute_mfma(kk, vv, sk, sv, tok0 - tg, end);
+      return;
+    }
     float x[NP * GB];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -407,6 +474,81 @@ struct Segment {
     PV<KV, NP, CPL, GB>::apply(sc, vv, acc);
   }
 
+  // The matrix-core path of compute (tile = one block; its first token blk_tok).
+  __device__ __forceinline__ void compute_mfma(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
+                                               const float (&sk)[NSC], const float (&sv)[NSC], int blk_tok, int end) {
+    const int lane = __lane_id();
+    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8_t b;
+      if constexpr (std::is_same<KV, __bf16>::value) {
+        const Chunk& c = kk[i / CPL][i % CPL];
+        b = as_bf16x8(c.w[0], c.w[1], c.w[2], c.w[3]);
+      } else {  // E4M3: codes 8 (i % 2) .. 8 (i % 2) + 7 of chunk i / 2, widened exactly
+        const Chunk& c = kk[(i >> 1) / CPL][(i >> 1) % CPL];
+        const int w = (i & 1) * 2;
+        b = as_bf16x8(fp8x2_to_bf16x2<false>(c.w[w]), fp8x2_to_bf16x2<true>(c.w[w]),
+                      fp8x2_to_bf16x2<false>(c.w[w + 1]), fp8x2_to_bf16x2<true>(c.w[w + 1]));
+      }
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], b, d, 0, 0, 0);
+    }
+    // lanes n < 16: the scores of token n for heads 0 .. 3 (rows 4 (l / 16) + h of the product)
+    const bool live = lane < 16 && blk_tok + lane < end;
+    const float fk = kScaled ? sk[0] * sl2 : sl2;
+    float s[GB], bm[GB];
+    bool need = false;
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      s[h] = live ? d[h] * fk : -__builtin_inff();
+      bm[h] = fmaxf(s[h], dpp_f32<0x128>(s[h]));  // tokens n and n + 8 share a running max
+      need |= bm[h] > mm[h] + kRescaleSlack;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        const float mn = fmaxf(mm[h], bm[h]);
+        const float alpha = fast_exp2(mm[h] - mn);
+        mm[h] = mn;
+        ml[h] *= alpha;
+        // the value lanes of group tg rescale by the factor of their group (lane tg)
+        const float av = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(tg << 2, __builtin_bit_cast(int, alpha)));
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[h][c][e] *= av;
+      }
+    }
+    float pv[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      const float pr = fast_exp2(s[h] - mm[h]);  // 0 for a masked token
+      ml[h] += pr;
+      // scaled caches: the token's V scale joins the weight (the sum keeps the plain one)
+      pv[h] = kScaled ? (live ? pr * sv[0] : 0.0f) : pr;
+    }
+    // each value lane takes the weights of its tokens tg and tg + 8
+    float prob[NP][GB];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int h = 0; h < GB; ++h)
+        prob[p][h] = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute((tg + 8 * p) << 2, __builtin_bit_cast(int, pv[h])));
+    PV<KV, NP, CPL, GB>::apply(prob, vv, acc);
+  }
+
+  // Matrix-core path: the group state of the value lanes from the score lanes
+  // (max of lane tg, sum of lanes tg and tg + 8), for merge_groups.
+  __device__ __forceinline__ void to_groups() {
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+      m[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(tg << 2, __builtin_bit_cast(int, mm[h])));
+      l[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(tg << 2, __builtin_bit_cast(int, ml[h]))) +
+             __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((tg + 8) << 2, __builtin_bit_cast(int, ml[h])));
+    }
+  }
+
   // Start from the attention state of a shared prefix: the a.init_splits
   // partials of rows [row, row + GB) (sequence * Hq + head) merged into token
   // group 0 (the other groups start empty; merge_groups combines them later).
@@ -471,7 +613,19 @@ struct Segment {
                                       int64_t seed_row = -1) {
     load_q(qrow);
     reset();
-    if (seed_row >= 0) seed(a, seed_row);
+    if (seed_row >= 0) {
+      seed(a, seed_row);
+      if constexpr (kMfmaK) {  // group 0 (tokens 0 and 8 of each block) starts from the prefix state
+        const int lane = __lane_id();
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+          const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(0, __builtin_bit_cast(int, m[h])));
+          const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(0, __builtin_bit_cast(int, l[h])));
+          mm[h] = (lane == 0 || lane == 8) ? m0 : kMaxInit;
+          ml[h] = lane == 0 ? l0 : 0.0f;
+        }
+      }
+    }
     const int64_t blk_stride = kTileBytes * a.num_kv_heads;
     const int num_blocks = a.num_blocks;
     // Table entries are uniform: scalar loads (the table is a read-only,
@@ -547,6 +701,7 @@ struct Segment {
       }
       if (jb + TB >= nblk) break;
     }
+    if constexpr (kMfmaK) to_groups();
   }
 
   // The token groups' outputs are combined by a reduce-scatter: each halving

@@ -16,6 +16,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxInit = -3.402823466e38f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
 
 struct alignas(16) Chunk {  // 16 bytes: 8 bf16 or 4 float32
   uint32_t w[4];

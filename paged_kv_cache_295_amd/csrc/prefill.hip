@@ -45,7 +45,6 @@
 
 namespace pkv {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -125,10 +124,6 @@ __host__ __device__ __forceinline__ int tile_rows(int chunk_len_max, int G) {
   return chunk_len_max * G <= kMRows ? chunk_len_max : kMRows / G;
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  uint4 u = make_uint4(a, b, c, d);
-  return __builtin_bit_cast(bf16x8_t, u);
-}
 
 // LDS reads in one asm block each, completed before the block ends; read i
 // is at base[i] + O.
