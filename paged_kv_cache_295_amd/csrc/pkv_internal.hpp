@@ -121,23 +121,32 @@ constexpr int heads_per_wave(int g) {
   return 1;
 }
 
-// Waves of the balanced decode split, by heads per wave and cache dtype.  One
-// wave per SIMD (1024 on the MI355X's 256 compute units) for float32 / bf16
-// caches with up to four heads per wave; a second wave per SIMD where the
-// vector work per byte is high -- eight heads per wave, or fp8 codes to widen --
-// so that one wave's arithmetic hides the other's memory waits.  Measured on
-// the Llama-3-8B batch with cold caches: fp8 61 us at 2048 waves against 90 us
-// at 1024; bf16 98 us at 2048 against 95 us at 1024 (four register stages).
+// Waves of the balanced decode split, by heads per wave, cache dtype and head
+// dim.  One wave per SIMD (1024 on the MI355X's 256 compute units) for
+// float32 / bf16 caches with up to four heads per wave; a second wave per SIMD
+// where the vector work per byte is high -- eight heads per wave, or fp8 codes
+// widened and dotted on the vector ALU -- so that one wave's arithmetic hides
+// the other's memory waits.  fp8 with four heads per wave at D = 128 takes its
+// scores on the matrix cores and is back to one wave per SIMD.  Measured on
+// the Llama-3-8B batch with cold caches: fp8 with vector-ALU scores 61 us at
+// 2048 waves against 90 us at 1024, with matrix-core scores 58.3 us at 2048
+// against 56.9 us at 1024; bf16 98 us at 2048 against 95 us at 1024 (four
+// register stages).
 #ifndef PKV_BALANCED_WAVES
 #define PKV_BALANCED_WAVES 0
 #endif
-constexpr int balanced_waves(int gb, int dtype) {
+constexpr int balanced_waves(int gb, int dtype, int head_dim) {
   if (PKV_BALANCED_WAVES > 0) return PKV_BALANCED_WAVES;
-  return (gb >= 8 || dtype == 2) ? 2048 : 1024;
+  if (gb >= 8) return 2048;
+  return (dtype == 2 && !(gb == 4 && head_dim == 128)) ? 2048 : 1024;
 }
-// The largest of them over the cache dtypes: what a workspace must hold.
+// The largest of them over the cache dtypes and head dims: what a workspace
+// must hold.
 constexpr int balanced_waves_max(int gb) {
-  return balanced_waves(gb, 2) > balanced_waves(gb, 1) ? balanced_waves(gb, 2) : balanced_waves(gb, 1);
+  int w = 0;
+  for (int dtype = 0; dtype <= 2; ++dtype)
+    for (int d = 64; d <= 128; d += 64) w = balanced_waves(gb, dtype, d) > w ? balanced_waves(gb, dtype, d) : w;
+  return w;
 }
 
 }  // namespace pkv
