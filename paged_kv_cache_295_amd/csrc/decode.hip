@@ -231,10 +231,11 @@ __device__ __forceinline__ void group_sum_all(float (&x)[N]) {
 // after the final normalisation.
 constexpr float kRescaleSlack = 8.0f;
 
-// bf16 caches take the matrix-core scores only with a deep register
-// pipeline: its longer chain per block (products, a lane exchange, the
-// softmax, ds_bpermute) is hidden by four blocks in flight but not by two (the
-// shared-prefix suffixes, two stages: 98.9 us per call with it, 94.3 without;
+// bf16 caches take the matrix-core segment only with a deep register
+// pipeline: its longer chain per block (score products, lane exchanges, the
+// softmax, the LDS copy of V, value products) is hidden by three or four
+// blocks in flight but not by two (the shared-prefix suffixes, two stages,
+// with the scores alone on the matrix cores: 98.9 us per call against 94.3;
 // the Llama-3-8B batch, four stages: 93.1 against 94.7 us).
 #ifndef PKV_DECODE_MFMA_BF16_MIN_STAGES
 #define PKV_DECODE_MFMA_BF16_MIN_STAGES 3
@@ -254,29 +255,35 @@ struct Segment {
   static constexpr int tok_of(int p) { return (p / PPB) * kBlock + (p % PPB) * TPP; }
   static constexpr int RB = S::kRowBytes;
   static constexpr bool kScaled = KvTraits<KV>::kScaled;
-  // scales carried per stage (one dummy entry when there are none)
-  static constexpr int NSC = kScaled ? NP : 1;
-
-  // Scores on the matrix cores (bf16 and E4M3 caches, D = 128, four query
-  // heads per wave): the scores of a block's 16 tokens are one chain of
-  // v_mfma_f32_16x16x32_bf16 over the head dims, heads as the rows (4 of the
-  // 16 used) and tokens as the columns, so no lane computes a partial dot
-  // product and no score is reduced across lanes.  Lane l = 16 q + n holds K
-  // bytes [64 j + 16 q, 64 j + 16 q + 16) of token n of the block (chunk j; the
-  // B operand of the products over those dims), and Q the same dims of head n
-  // (the A operand; zero rows for n >= 4).  The scores land in lanes n < 16,
-  // four heads each; there the softmax runs once per (token, head) with the
-  // running max shared by tokens n and n + 8 (the two tokens a value lane
-  // holds), and ds_bpermute hands each value lane its two tokens' weights.
-  static constexpr bool kMfmaK =
+  // The matrix-core segment (bf16 and E4M3 caches, D = 128, four query heads
+  // per wave).  Scores: S = K Q^T for the block's 16 tokens is one chain of
+  // four v_mfma_f32_16x16x32_bf16 products over the head dims, tokens as rows
+  // and heads as columns (4 of 16 used): lane l = 16 g + n loads K bytes
+  // [64 j + 16 g, +16) of token n (so a load covers 64 contiguous bytes of 16
+  // rows) and holds Q^T's same dims for head n, and ends with the scores of
+  // tokens 4 g .. 4 g + 3 for head n.  The softmax runs there, one running max
+  // per head for the whole block (the four lane groups agree on it through two
+  // lane swaps), so every token of a head accumulates at the same scale.
+  // Values: O^T += V^T P^T is eight v_mfma_f32_16x16x16_bf16 products, one per
+  // 16 dims, with P^T (bf16) straight from the score lanes (lane 16 g + n holds
+  // the weights of tokens 4 g .. 4 g + 3 for head n, the B operand) and V^T
+  // read from the wave's LDS copy of the block with ds_read_b64_tr_b16 (lane
+  // j of group g addresses token 4 g + j / 4, dims 4 (j % 4) of a 16-dim slice,
+  // and lane i receives dim i of tokens 4 g .. 4 g + 3); the copy's 8-byte
+  // units are XOR-swizzled by token so that those reads hit distinct banks.
+  // No partial dot products, no score reductions, no token groups to merge.
+  static constexpr bool kMfma =
       (std::is_same<KV, Fp8E4M3>::value || (std::is_same<KV, __bf16>::value && NS >= PKV_DECODE_MFMA_BF16_MIN_STAGES)) &&
       D == 128 && GB == 4 && LPT == 8;
   static constexpr int kKC = RB / 64;  // K chunks per lane per block
-  static_assert(!kMfmaK || (BPT == 1 && NP * CPL == kKC && NP == 2 && TPP == 8), "one block per tile");
+  static_assert(!kMfma || (BPT == 1 && NP * CPL == kKC && NP == 2 && TPP == 8), "one block per tile");
+  // scales carried per stage (one dummy entry when there are none)
+  static constexpr int NSC = kScaled ? (kMfma ? 4 : NP) : 1;
 
   Chunk qv[GB][CPL][QPC];
-  bf16x8_t qa[4];        // matrix-core path: Q as the A operand of the four products
-  float mm[GB], ml[GB];  // matrix-core path: running max / sum of token n's group, lanes n < 16
+  bf16x8_t qa[4];        // matrix-core segment: Q^T, the B operand of the four score products
+  float mh, lh;          // matrix-core segment: running max / sum of head lane % 16 (this lane's tokens)
+  f32x4_t oacc[D / 16];  // matrix-core segment: O^T, lane l: head l % 16, dims 16 t + 4 (l / 16) + i
   float m[GB], l[GB], acc[GB][CPL][EPC];
   bool bad_block;
   int tg, li;
@@ -303,7 +310,7 @@ struct Segment {
 
   // The chunks of the GB query rows at qrow (head h0 of the row) this lane multiplies.
   __device__ __forceinline__ void load_q(const T* __restrict__ qrow) {
-    if constexpr (kMfmaK) {
+    if constexpr (kMfma) {
       const int lane = __lane_id();
       const int hm = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -329,14 +336,19 @@ struct Segment {
     for (int h = 0; h < GB; ++h) {
       m[h] = kMaxInit;
       l[h] = 0.0f;
-      mm[h] = kMaxInit;
-      ml[h] = 0.0f;
+
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[h][c][e] = 0.0f;
     }
     bad_block = false;
+    if constexpr (kMfma) {
+      mh = kMaxInit;
+      lh = 0.0f;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) oacc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
   }
 
   // The K and V tiles (16 tokens of one kv head each) of the BPT blocks of a
@@ -351,7 +363,7 @@ struct Segment {
                                             float (&sv)[NSC], const int64_t (&off)[BPT],
                                             const int (&nbytes)[BPT]) const {
     constexpr int kAux = kStreamKV ? 2 : 0;  // cache policy: bit 1 = non-temporal
-    if constexpr (kMfmaK) {
+    if constexpr (kMfma) {
       const int lane = __lane_id();
       const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kc + off[0], nbytes[0]);
       const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vc + off[0], nbytes[0]);
@@ -365,10 +377,12 @@ struct Segment {
         for (int c = 0; c < CPL; ++c)
           vv[pp][c] = as_chunk(
               __builtin_amdgcn_raw_buffer_load_b128(vr, lane_base + pp * TPP * RB + c * LPT * 16, 0, kAux));
-      if constexpr (kScaled) {  // the scales of token n = lane % 16
-        const int64_t so = off[0] / RB + (lane & 15);
-        sk[0] = __builtin_nontemporal_load(ksc + so);
-        sv[0] = __builtin_nontemporal_load(vsc + so);
+      if constexpr (kScaled) {  // the scales of this lane's tokens 4 g .. 4 g + 3 (one 16-byte row piece)
+        const int64_t so = off[0] / RB + 4 * (lane >> 4);
+        const float4 k4 = *reinterpret_cast<const float4*>(ksc + so);
+        const float4 v4 = *reinterpret_cast<const float4*>(vsc + so);
+        sk[0] = k4.x; sk[1] = k4.y; sk[2] = k4.z; sk[3] = k4.w;
+        sv[0] = v4.x; sv[1] = v4.y; sv[2] = v4.z; sv[3] = v4.w;
       }
       return;
     }
@@ -403,7 +417,7 @@ struct Segment {
   // paths cost the register pipeline its fixed placement.)
   __device__ __forceinline__ void compute(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
                                           const float (&sk)[NSC], const float (&sv)[NSC], int tok0, int end) {
-    if constexpr (kMfmaK) {
+    if constexpr (kMfma) {
       compute_mfma(kk, vv, sk, sv, tok0 - tg, end);
       return;
     }
@@ -474,79 +488,122 @@ struct Segment {
     PV<KV, NP, CPL, GB>::apply(sc, vv, acc);
   }
 
-  // The matrix-core path of compute (tile = one block; its first token blk_tok).
+  // The matrix-core segment's block (tile = one block; its first token blk_tok).
   __device__ __forceinline__ void compute_mfma(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
                                                const float (&sk)[NSC], const float (&sv)[NSC], int blk_tok, int end) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    // one 16-token x 128-dim bf16 V tile per wave (the workgroup is the wave)
+    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kBlock * D];
     const int lane = __lane_id();
+    const int n = lane & 15, g = lane >> 4;
+    // 8-byte unit u (dims 4u .. 4u + 3) of token t sits at unit u ^ swz(t)
+    auto swz = [](int t) { return 4 * (t & 3) ^ 16 * ((t >> 2) & 1); };
+
+    // V tile -> LDS as bf16 (value lane (tg, li) holds tokens tg and tg + 8)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int t = tg + 8 * p;
+      char* row = reinterpret_cast<char*>(vt_lds) + t * (D * 2);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if constexpr (std::is_same<KV, __bf16>::value) {  // 8 dims: units 2 (8 c + li), +1
+          const int u = 2 * (c * LPT + li);
+          *reinterpret_cast<uint4*>(row + (u ^ swz(t)) * 8) =
+              make_uint4(vv[p][c].w[0], vv[p][c].w[1], vv[p][c].w[2], vv[p][c].w[3]);
+        } else {  // 16 codes (dims 16 li .. 16 li + 15) widened: units 4 li .. 4 li + 3
+          const Chunk& v = vv[p][c];
+          const int u = 4 * li;
+          *reinterpret_cast<uint4*>(row + (u ^ swz(t)) * 8) =
+              make_uint4(fp8x2_to_bf16x2<false>(v.w[0]), fp8x2_to_bf16x2<true>(v.w[0]),
+                         fp8x2_to_bf16x2<false>(v.w[1]), fp8x2_to_bf16x2<true>(v.w[1]));
+          *reinterpret_cast<uint4*>(row + ((u + 2) ^ swz(t)) * 8) =
+              make_uint4(fp8x2_to_bf16x2<false>(v.w[2]), fp8x2_to_bf16x2<true>(v.w[2]),
+                         fp8x2_to_bf16x2<false>(v.w[3]), fp8x2_to_bf16x2<true>(v.w[3]));
+        }
+      }
+    }
+
+    // scores S[token 4 g + i][head n]
     f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bf16x8_t b;
+      bf16x8_t a;
       if constexpr (std::is_same<KV, __bf16>::value) {
         const Chunk& c = kk[i / CPL][i % CPL];
-        b = as_bf16x8(c.w[0], c.w[1], c.w[2], c.w[3]);
+        a = as_bf16x8(c.w[0], c.w[1], c.w[2], c.w[3]);
       } else {  // E4M3: codes 8 (i % 2) .. 8 (i % 2) + 7 of chunk i / 2, widened exactly
         const Chunk& c = kk[(i >> 1) / CPL][(i >> 1) % CPL];
         const int w = (i & 1) * 2;
-        b = as_bf16x8(fp8x2_to_bf16x2<false>(c.w[w]), fp8x2_to_bf16x2<true>(c.w[w]),
+        a = as_bf16x8(fp8x2_to_bf16x2<false>(c.w[w]), fp8x2_to_bf16x2<true>(c.w[w]),
                       fp8x2_to_bf16x2<false>(c.w[w + 1]), fp8x2_to_bf16x2<true>(c.w[w + 1]));
       }
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], b, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qa[i], d, 0, 0, 0);
     }
-    // lanes n < 16: the scores of token n for heads 0 .. 3 (rows 4 (l / 16) + h of the product)
-    const bool live = lane < 16 && blk_tok + lane < end;
-    const float fk = kScaled ? sk[0] * sl2 : sl2;
-    float s[GB], bm[GB];
-    bool need = false;
+    float s[4], bm = -__builtin_inff();
 #pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      s[h] = live ? d[h] * fk : -__builtin_inff();
-      bm[h] = fmaxf(s[h], dpp_f32<0x128>(s[h]));  // tokens n and n + 8 share a running max
-      need |= bm[h] > mm[h] + kRescaleSlack;
+    for (int i = 0; i < 4; ++i) {
+      const bool live = n < GB && blk_tok + 4 * g + i < end;
+      s[i] = live ? d[i] * (kScaled ? sk[kScaled ? i : 0] * sl2 : sl2) : -__builtin_inff();
+      bm = fmaxf(bm, s[i]);
     }
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+    bm = xor_max<32>(xor_max<16>(bm));  // the block max of head n, in all four lane groups
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bm > mh + kRescaleSlack) != 0, 0)) {
+      const float mn = fmaxf(mh, bm);
+      const float alpha = fast_exp2(mh - mn);
+      mh = mn;
+      lh *= alpha;
 #pragma unroll
-      for (int h = 0; h < GB; ++h) {
-        const float mn = fmaxf(mm[h], bm[h]);
-        const float alpha = fast_exp2(mm[h] - mn);
-        mm[h] = mn;
-        ml[h] *= alpha;
-        // the value lanes of group tg rescale by the factor of their group (lane tg)
-        const float av = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(tg << 2, __builtin_bit_cast(int, alpha)));
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[h][c][e] *= av;
-      }
+      for (int t = 0; t < D / 16; ++t) oacc[t] *= alpha;
     }
-    float pv[GB];
+    float pv[4];
 #pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      const float pr = fast_exp2(s[h] - mm[h]);  // 0 for a masked token
-      ml[h] += pr;
+    for (int i = 0; i < 4; ++i) {
+      const float pr = fast_exp2(s[i] - mh);  // 0 for a masked token or a padding head
+      lh += pr;
       // scaled caches: the token's V scale joins the weight (the sum keeps the plain one)
-      pv[h] = kScaled ? (live ? pr * sv[0] : 0.0f) : pr;
+      pv[i] = kScaled ? (s[i] > -__builtin_inff() ? pr * sv[kScaled ? i : 0] : 0.0f) : pr;
     }
-    // each value lane takes the weights of its tokens tg and tg + 8
-    float prob[NP][GB];
+    const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
+    const s16x4_t pt = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+
+    // O^T[16 t .. 16 t + 15][head] += V^T P^T
+    const int tt = 4 * g + (n >> 2);  // the token this lane addresses for the transposing reads
+    const char* rrow = reinterpret_cast<const char*>(vt_lds) + tt * (D * 2);
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int h = 0; h < GB; ++h)
-        prob[p][h] = __builtin_bit_cast(
-            float, __builtin_amdgcn_ds_bpermute((tg + 8 * p) << 2, __builtin_bit_cast(int, pv[h])));
-    PV<KV, NP, CPL, GB>::apply(prob, vv, acc);
+    for (int t = 0; t < D / 16; ++t) {
+      const int u = 4 * t + (n & 3);
+      const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(rrow + (u ^ swz(tt)) * 8));
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, oacc[t], 0, 0, 0);
+    }
   }
 
-  // Matrix-core path: the group state of the value lanes from the score lanes
-  // (max of lane tg, sum of lanes tg and tg + 8), for merge_groups.
-  __device__ __forceinline__ void to_groups() {
-#pragma unroll
-    for (int h = 0; h < GB; ++h) {
-      m[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(tg << 2, __builtin_bit_cast(int, mm[h])));
-      l[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(tg << 2, __builtin_bit_cast(int, ml[h]))) +
-             __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((tg + 8) << 2, __builtin_bit_cast(int, ml[h])));
+  // seed() for the matrix-core segment: lane 16 g + n (n < GB) takes head n's
+  // prefix max, its output dims 16 t + 4 g + i, and (group 0 only) its sum.
+  __device__ __forceinline__ void seed_mfma(const DecodeArgs& a, int64_t row0) {
+    const int lane = __lane_id();
+    const int n = lane & 15, g = lane >> 4;
+    if (n >= GB) return;
+    const int64_t split_stride = (int64_t)a.num_seqs * a.num_q_heads;
+    float M = kMaxInit;
+    for (int sp = 0; sp < a.init_splits; ++sp) {
+      const float ms = a.init_ml[(sp * split_stride + row0 + n) * 2];
+      bad_block |= ms != ms;
+      M = fmaxf(M, ms);
     }
+    float lam = 0.0f;
+    for (int sp = 0; sp < a.init_splits; ++sp) {
+      const int64_t r = sp * split_stride + row0 + n;
+      const float f = fast_exp2(a.init_ml[r * 2] - M);
+      lam = fmaf(f, a.init_ml[r * 2 + 1], lam);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const float4 v = *reinterpret_cast<const float4*>(a.init_o + r * D + 16 * t + 4 * g);
+        oacc[t] += f32x4_t{f * v.x, f * v.y, f * v.z, f * v.w};
+      }
+    }
+    mh = M;
+    lh = g == 0 ? lam : 0.0f;
   }
 
   // Start from the attention state of a shared prefix: the a.init_splits
@@ -614,17 +671,10 @@ struct Segment {
     load_q(qrow);
     reset();
     if (seed_row >= 0) {
-      seed(a, seed_row);
-      if constexpr (kMfmaK) {  // group 0 (tokens 0 and 8 of each block) starts from the prefix state
-        const int lane = __lane_id();
-#pragma unroll
-        for (int h = 0; h < GB; ++h) {
-          const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(0, __builtin_bit_cast(int, m[h])));
-          const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(0, __builtin_bit_cast(int, l[h])));
-          mm[h] = (lane == 0 || lane == 8) ? m0 : kMaxInit;
-          ml[h] = lane == 0 ? l0 : 0.0f;
-        }
-      }
+      if constexpr (kMfma)
+        seed_mfma(a, seed_row);
+      else
+        seed(a, seed_row);
     }
     const int64_t blk_stride = kTileBytes * a.num_kv_heads;
     const int num_blocks = a.num_blocks;
@@ -701,7 +751,6 @@ struct Segment {
       }
       if (jb + TB >= nblk) break;
     }
-    if constexpr (kMfmaK) to_groups();
   }
 
   // The token groups' outputs are combined by a reduce-scatter: each halving
@@ -756,6 +805,10 @@ struct Segment {
   __device__ __forceinline__ void merge_groups() {
     static_assert(LPT == 4 || LPT == 8 || LPT == 16, "token groups differ in lane bits 2..5, 3..5 or 4..5");
     bad_block = __builtin_amdgcn_ballot_w64(bad_block) != 0;
+    if constexpr (kMfma) {  // one running max per head already; the sums of the four lane groups
+      lh = xor_add<32>(xor_add<16>(lh));
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
       const float M = groups_max<LPT>(m[h]);
@@ -788,6 +841,18 @@ struct Segment {
   // Normalised output of the GB heads at outp (head h0 of the row).
   __device__ __forceinline__ void store_out(T* __restrict__ outp) {
     const float nan = __builtin_nanf("");
+    if constexpr (kMfma) {  // lane 16 g + n (n < GB): dims 16 t + 4 g .. + 3 of head n
+      const int lane = __lane_id();
+      const int n = lane & 15, g = lane >> 4;
+      if (n < GB) {
+        const float inv = bad_block ? nan : 1.0f / lh;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+          *reinterpret_cast<uint2*>(outp + n * D + 16 * t + 4 * g) =
+              make_uint2(pack_bf16x2(oacc[t][0] * inv, oacc[t][1] * inv), pack_bf16x2(oacc[t][2] * inv, oacc[t][3] * inv));
+      }
+      return;
+    }
     if constexpr (kScatter) {
       // normalise per head first (every head's sum is in every lane), then scatter
 #pragma unroll
@@ -836,6 +901,21 @@ struct Segment {
   __device__ __forceinline__ void store_partial(float* __restrict__ po, int64_t ostride, float* __restrict__ pml,
                                                 int64_t mlstride) {
     const float nan = __builtin_nanf("");
+    if constexpr (kMfma) {
+      const int lane = __lane_id();
+      const int n = lane & 15, g = lane >> 4;
+      if (n < GB) {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+          *reinterpret_cast<float4*>(po + n * ostride + 16 * t + 4 * g) =
+              make_float4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3]);
+        if (g == 0) {
+          pml[n * mlstride] = bad_block ? nan : mh;
+          pml[n * mlstride + 1] = lh;
+        }
+      }
+      return;
+    }
     if constexpr (kScatter) {
       scatter();
 #pragma unroll
@@ -1541,16 +1621,19 @@ constexpr int lanes_per_token() {
   return row_chunks < want ? row_chunks : want;
 }
 // Register stages of the K/V prefetch pipeline.  bf16 with up to four heads
-// per wave runs at one wave per SIMD; for long contexts it keeps four blocks in
-// flight (cold caches, the Llama-3-8B batch: 95-98 us against 102 us with two),
-// while short ones keep two, whose pipeline fills faster at every segment start
-// (the shared-prefix suffixes of at most 512 tokens: 101 us against 110 us).
-// The types and groups that run two waves per SIMD, or need the registers
-// (float32), keep two.
+// per wave runs at one wave per SIMD; for long contexts it keeps more blocks in
+// flight (cold caches, the Llama-3-8B batch: 95-98 us with four against 102 us
+// with two on the vector-ALU segment; on the matrix-core segment three beat
+// four, 89.8 against 90.6 us), while short ones keep two, whose pipeline fills
+// faster at every segment start (the shared-prefix suffixes of at most 512
+// tokens: 101 us against 110 us).  E4M3 on the matrix-core segment takes three
+// as well (56.4 against 57.6 us with two, 57.3 with four).  The types and
+// groups that run two waves per SIMD, or need the registers (float32), keep two.
 template <typename KV, int D, int GB>
 constexpr int deep_stages() {
   if (PKV_DECODE_STAGES > 0) return PKV_DECODE_STAGES;
-  return (std::is_same<KV, __bf16>::value && GB <= 4) ? 4 : 2;
+  if (std::is_same<KV, Fp8E4M3>::value) return (D == 128 && GB == 4) ? 3 : 2;
+  return (std::is_same<KV, __bf16>::value && GB <= 4) ? 3 : 2;
 }
 constexpr int kDeepPipelineMinTokens = 1024;  // longest context from which the deep pipeline pays
 
