@@ -400,9 +400,9 @@ def main():
         # What this access pattern allows: the read probe loads every K/V row the
         # decode call reads, with its loads, over the same wavefront count, and
         # computes nothing (paged_kv_read_probe).
-        # (an fp8 cache runs twice the bf16 count unless a wave takes four heads at D = 128)
+        # (an fp8 cache runs twice the bf16 count unless a wave takes four or eight heads at D = 128)
         gb = next(x for x in (8, 4, 2, 1) if (w.num_q_heads // w.num_kv_heads) % x == 0)
-        fp8_twice = fp8 and not (gb == 4 and w.head_dim == 128)
+        fp8_twice = fp8 and not (gb in (4, 8) and w.head_dim == 128)
         waves = pkv.decode_split_waves(w.num_q_heads, w.num_kv_heads) * (2 if fp8_twice else 1)
         pwords = torch.empty(waves, dtype=torch.int32, device=dev)
         probe = (lambda: pkv.paged_kv_read_probe(kc, vc, tables, lens, waves, pwords, k_scale=ksc, v_scale=vsc)) \

@@ -204,10 +204,12 @@ int paged_block_release(const int32_t* table, int32_t num_table_blocks, int32_t*
  *
  *   partition_tokens == 0 (recommended): balanced split.  The whole batch's
  *     work -- every (sequence, kv head, 16-token block) -- is divided over
- *     paged_attn_decode_split_waves(num_q_heads, num_kv_heads) wavefronts (for
- *     float32 / bf16 caches; fp8 caches use twice as many when that count is
- *     1024, except with four query heads per kv head at head_dim 128) in runs
- *     of consecutive blocks.  Each (sequence, kv head) stream is
+ *     wavefronts in runs of consecutive blocks:
+ *     paged_attn_decode_split_waves(num_q_heads, num_kv_heads) of them for a
+ *     bf16 cache whose longest context (max_context_len) reaches 1024 tokens;
+ *     otherwise 1024 or 2048 as the arithmetic per byte needs (2048 where the
+ *     vector ALU computes the scores of eight heads per wave or of E4M3
+ *     codes).  Each (sequence, kv head) stream is
  *     charged its blocks plus a fixed cost for starting it, and every wavefront
  *     gets the same total charge, so all finish together whatever the mix of
  *     context lengths; a context is cut wherever a run ends.  The workspace

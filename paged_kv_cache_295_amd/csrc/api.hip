@@ -199,7 +199,7 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* cac
 
 int32_t paged_attn_decode_split_waves(int32_t num_q_heads, int32_t num_kv_heads) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
-  return balanced_waves(heads_per_wave(num_q_heads / num_kv_heads), PKV_DTYPE_BF16, 128);
+  return balanced_waves(heads_per_wave(num_q_heads / num_kv_heads), PKV_DTYPE_BF16, 128, kDeepPipelineMinTokens);
 }
 
 int paged_kv_read_probe(const void* k_cache, const void* v_cache, const pkv_cache_desc* cache,
@@ -275,7 +275,7 @@ int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const vo
   const int gb = heads_per_wave(num_q_heads / cache->num_kv_heads);
   const int64_t streams = (int64_t)num_seqs * cache->num_kv_heads * ((num_q_heads / cache->num_kv_heads) / gb);
   const bool whole = balanced && streams * (((int64_t)max_context_len + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE) <=
-                                     balanced_waves(gb, cache->dtype, cache->head_dim);
+                                     balanced_waves(gb, cache->dtype, cache->head_dim, max_context_len);
   DecodeArgs a{};
   a.q = q;
   a.out = out;
@@ -298,7 +298,7 @@ int decode_common(const void* q, int32_t num_seqs, int32_t num_q_heads, const vo
   a.partition_tokens = part;
   a.max_parts = (int32_t)max_parts64;
   a.scale_log2 = scale * kLog2eHost;
-  a.balanced_waves = balanced && !whole ? balanced_waves(gb, cache->dtype, cache->head_dim) : 0;
+  a.balanced_waves = balanced && !whole ? balanced_waves(gb, cache->dtype, cache->head_dim, max_context_len) : 0;
   a.max_context_tokens = max_context_len;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
@@ -513,7 +513,7 @@ int paged_attn_decode_shared_prefix(const void* q, int32_t num_seqs, int32_t num
   a.max_parts = 1;
   a.scale_log2 = sl2;
   a.balanced_waves =
-      balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads), cache->dtype, cache->head_dim);
+      balanced_waves(heads_per_wave(num_q_heads / cache->num_kv_heads), cache->dtype, cache->head_dim, 0);
   if (prefix_len > 0) {
     a.init_o = pre_o;
     a.init_ml = pre_o + (size_t)ps.splits * num_seqs * num_q_heads * cache->head_dim;

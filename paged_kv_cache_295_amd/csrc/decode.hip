@@ -255,10 +255,10 @@ struct Segment {
   static constexpr int tok_of(int p) { return (p / PPB) * kBlock + (p % PPB) * TPP; }
   static constexpr int RB = S::kRowBytes;
   static constexpr bool kScaled = KvTraits<KV>::kScaled;
-  // The matrix-core segment (bf16 and E4M3 caches, D = 128, four query heads
-  // per wave).  Scores: S = K Q^T for the block's 16 tokens is one chain of
-  // four v_mfma_f32_16x16x32_bf16 products over the head dims, tokens as rows
-  // and heads as columns (4 of 16 used): lane l = 16 g + n loads K bytes
+  // The matrix-core segment (bf16 and E4M3 caches, D = 128, four or eight
+  // query heads per wave).  Scores: S = K Q^T for the block's 16 tokens is one
+  // chain of four v_mfma_f32_16x16x32_bf16 products over the head dims, tokens
+  // as rows and heads as columns (4 or 8 of 16 used): lane l = 16 g + n loads K bytes
   // [64 j + 16 g, +16) of token n (so a load covers 64 contiguous bytes of 16
   // rows) and holds Q^T's same dims for head n, and ends with the scores of
   // tokens 4 g .. 4 g + 3 for head n.  The softmax runs there, one running max
@@ -274,9 +274,9 @@ struct Segment {
   // No partial dot products, no score reductions, no token groups to merge.
   static constexpr bool kMfma =
       (std::is_same<KV, Fp8E4M3>::value || (std::is_same<KV, __bf16>::value && NS >= PKV_DECODE_MFMA_BF16_MIN_STAGES)) &&
-      D == 128 && GB == 4 && LPT == 8;
+      D == 128 && (GB == 4 || GB == 8);
   static constexpr int kKC = RB / 64;  // K chunks per lane per block
-  static_assert(!kMfma || (BPT == 1 && NP * CPL == kKC && NP == 2 && TPP == 8), "one block per tile");
+  static_assert(!kMfma || (BPT == 1 && NP * CPL == kKC && TPP * NP == kBlock), "one block per tile");
   // scales carried per stage (one dummy entry when there are none)
   static constexpr int NSC = kScaled ? (kMfma ? 4 : NP) : 1;
 
@@ -499,10 +499,10 @@ struct Segment {
     // 8-byte unit u (dims 4u .. 4u + 3) of token t sits at unit u ^ swz(t)
     auto swz = [](int t) { return 4 * (t & 3) ^ 16 * ((t >> 2) & 1); };
 
-    // V tile -> LDS as bf16 (value lane (tg, li) holds tokens tg and tg + 8)
+    // V tile -> LDS as bf16 (value lane (tg, li) holds tokens tg + TPP p)
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int t = tg + 8 * p;
+      const int t = tg + TPP * p;
       char* row = reinterpret_cast<char*>(vt_lds) + t * (D * 2);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -510,9 +510,9 @@ struct Segment {
           const int u = 2 * (c * LPT + li);
           *reinterpret_cast<uint4*>(row + (u ^ swz(t)) * 8) =
               make_uint4(vv[p][c].w[0], vv[p][c].w[1], vv[p][c].w[2], vv[p][c].w[3]);
-        } else {  // 16 codes (dims 16 li .. 16 li + 15) widened: units 4 li .. 4 li + 3
+        } else {  // 16 codes (dims 16 (c LPT + li) .. + 15) widened: four units
           const Chunk& v = vv[p][c];
-          const int u = 4 * li;
+          const int u = 4 * (c * LPT + li);
           *reinterpret_cast<uint4*>(row + (u ^ swz(t)) * 8) =
               make_uint4(fp8x2_to_bf16x2<false>(v.w[0]), fp8x2_to_bf16x2<true>(v.w[0]),
                          fp8x2_to_bf16x2<false>(v.w[1]), fp8x2_to_bf16x2<true>(v.w[1]));
@@ -1632,10 +1632,11 @@ constexpr int lanes_per_token() {
 template <typename KV, int D, int GB>
 constexpr int deep_stages() {
   if (PKV_DECODE_STAGES > 0) return PKV_DECODE_STAGES;
-  if (std::is_same<KV, Fp8E4M3>::value) return (D == 128 && GB == 4) ? 3 : 2;
-  return (std::is_same<KV, __bf16>::value && GB <= 4) ? 3 : 2;
+  constexpr bool matrix = D == 128 && (GB == 4 || GB == 8);  // the matrix-core segment
+  if (std::is_same<KV, Fp8E4M3>::value) return matrix ? 3 : 2;
+  if (std::is_same<KV, __bf16>::value) return matrix ? 3 : (GB <= 4 ? 4 : 2);
+  return 2;
 }
-constexpr int kDeepPipelineMinTokens = 1024;  // longest context from which the deep pipeline pays
 
 // Merge grids of at most this many waves take one head per wave.
 constexpr int64_t kMergeWavesPerHead = 4096;

@@ -121,31 +121,45 @@ constexpr int heads_per_wave(int g) {
   return 1;
 }
 
-// Waves of the balanced decode split, by heads per wave, cache dtype and head
-// dim.  One wave per SIMD (1024 on the MI355X's 256 compute units) for
-// float32 / bf16 caches with up to four heads per wave; a second wave per SIMD
-// where the vector work per byte is high -- eight heads per wave, or fp8 codes
-// widened and dotted on the vector ALU -- so that one wave's arithmetic hides
-// the other's memory waits.  fp8 with four heads per wave at D = 128 takes its
-// scores on the matrix cores and is back to one wave per SIMD.  Measured on
-// the Llama-3-8B batch with cold caches: fp8 with vector-ALU scores 61 us at
-// 2048 waves against 90 us at 1024, with matrix-core scores 58.3 us at 2048
-// against 56.9 us at 1024; bf16 98 us at 2048 against 95 us at 1024 (four
-// register stages).
+// Longest context from which the decode keeps more than two blocks in
+// flight per wave (and bf16 caches take the matrix-core segment).
+constexpr int kDeepPipelineMinTokens = 1024;
+
+// Whether a decode runs the matrix-core segment (scores and value products on
+// the matrix cores): D = 128 with four or eight heads per wave, E4M3 caches
+// always, bf16 caches with the deep pipeline.
+constexpr bool matrix_segment(int gb, int dtype, int head_dim, int max_context_tokens) {
+  return head_dim == 128 && (gb == 4 || gb == 8) &&
+         (dtype == 2 || (dtype == 1 && max_context_tokens >= kDeepPipelineMinTokens));
+}
+
+// Waves of the balanced decode split.  One wave per SIMD (1024 on the
+// MI355X's 256 compute units) wherever the matrix-core segment runs, and for
+// float32 / bf16 caches with up to four heads per wave on the vector-ALU
+// segment; a second wave per SIMD where the vector-ALU segment's work per byte
+// is high -- eight heads per wave, or fp8 codes widened and dotted on the
+// vector ALU -- so that one wave's arithmetic hides the other's memory waits.
+// Measured with cold caches: the Llama-3-8B batch on the E4M3 cache, vector
+// ALU 61 us at 2048 waves against 90 us at 1024, matrix cores 56.9 us at 1024
+// against 58.3 us at 2048; bf16 on the vector ALU 98 us at 2048 against 95 us
+// at 1024; the long-context batch (eight heads per wave) on the matrix cores
+// 458.5 us at 1024 against 479.7 us at 2048.
 #ifndef PKV_BALANCED_WAVES
 #define PKV_BALANCED_WAVES 0
 #endif
-constexpr int balanced_waves(int gb, int dtype, int head_dim) {
+constexpr int balanced_waves(int gb, int dtype, int head_dim, int max_context_tokens) {
   if (PKV_BALANCED_WAVES > 0) return PKV_BALANCED_WAVES;
-  if (gb >= 8) return 2048;
-  return (dtype == 2 && !(gb == 4 && head_dim == 128)) ? 2048 : 1024;
+  if (matrix_segment(gb, dtype, head_dim, max_context_tokens)) return 1024;
+  return (gb >= 8 || dtype == 2) ? 2048 : 1024;
 }
-// The largest of them over the cache dtypes and head dims: what a workspace
-// must hold.
+// The largest of them over the cache dtypes, head dims and context lengths:
+// what a workspace must hold.
 constexpr int balanced_waves_max(int gb) {
   int w = 0;
   for (int dtype = 0; dtype <= 2; ++dtype)
-    for (int d = 64; d <= 128; d += 64) w = balanced_waves(gb, dtype, d) > w ? balanced_waves(gb, dtype, d) : w;
+    for (int d = 64; d <= 128; d += 64)
+      for (int ctx = 0; ctx <= kDeepPipelineMinTokens; ctx += kDeepPipelineMinTokens)
+        w = balanced_waves(gb, dtype, d, ctx) > w ? balanced_waves(gb, dtype, d, ctx) : w;
   return w;
 }
 

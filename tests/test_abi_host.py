@@ -102,11 +102,12 @@ def test_decode_validation(lib):
 
 def test_workspace_sizes(lib):
     # balanced split: [waves][2 slots][heads per wave][D + 2] floats, independent of the contexts; sized
-    # for the larger wave count over the cache dtypes (2048: fp8 caches and eight heads per wave run two
-    # waves per SIMD), the bf16 count is what split_waves reports
+    # for the largest wave count over cache dtypes, head dims and context lengths (2048: the vector-ALU
+    # segment with eight heads per wave or fp8 codes runs two waves per SIMD); split_waves reports the
+    # count for a bf16 cache with contexts of 1024 tokens or more (one wave per SIMD)
     for (hq, hkv, gb) in [(32, 8, 4), (64, 8, 8), (8, 8, 1), (24, 4, 2), (12, 4, 1), (128, 8, 8)]:
         W = lib.paged_attn_decode_split_waves(hq, hkv)
-        assert W == (2048 if gb == 8 else 1024)
+        assert W == 1024
         for L in (1, 4096, 131072):
             assert lib.paged_attn_decode_workspace_bytes(3, hq, hkv, 128, L, 0) == 2048 * 2 * gb * 130 * 4
     assert lib.paged_attn_decode_split_waves(12, 8) == 0
