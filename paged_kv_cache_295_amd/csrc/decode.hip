@@ -578,34 +578,6 @@ struct Segment {
     }
   }
 
-  // seed() for the matrix-core segment: lane 16 g + n (n < GB) takes head n's
-  // prefix max, its output dims 16 t + 4 g + i, and (group 0 only) its sum.
-  __device__ __forceinline__ void seed_mfma(const DecodeArgs& a, int64_t row0) {
-    const int lane = __lane_id();
-    const int n = lane & 15, g = lane >> 4;
-    if (n >= GB) return;
-    const int64_t split_stride = (int64_t)a.num_seqs * a.num_q_heads;
-    float M = kMaxInit;
-    for (int sp = 0; sp < a.init_splits; ++sp) {
-      const float ms = a.init_ml[(sp * split_stride + row0 + n) * 2];
-      bad_block |= ms != ms;
-      M = fmaxf(M, ms);
-    }
-    float lam = 0.0f;
-    for (int sp = 0; sp < a.init_splits; ++sp) {
-      const int64_t r = sp * split_stride + row0 + n;
-      const float f = fast_exp2(a.init_ml[r * 2] - M);
-      lam = fmaf(f, a.init_ml[r * 2 + 1], lam);
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const float4 v = *reinterpret_cast<const float4*>(a.init_o + r * D + 16 * t + 4 * g);
-        oacc[t] += f32x4_t{f * v.x, f * v.y, f * v.z, f * v.w};
-      }
-    }
-    mh = M;
-    lh = g == 0 ? lam : 0.0f;
-  }
-
   // Start from the attention state of a shared prefix: the a.init_splits
   // partials of rows [row, row + GB) (sequence * Hq + head) merged into token
   // group 0 (the other groups start empty; merge_groups combines them later).
@@ -671,8 +643,11 @@ struct Segment {
     load_q(qrow);
     reset();
     if (seed_row >= 0) {
+      // The shared-prefix call runs the two-stage vector-ALU segment, which
+      // takes a seed; the matrix-core segment has none and would drop the
+      // prefix, so it marks the row bad (NaN) instead.
       if constexpr (kMfma)
-        seed_mfma(a, seed_row);
+        bad_block = true;
       else
         seed(a, seed_row);
     }
