@@ -58,6 +58,17 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_295_amd", "csrc")
 DECODE_SOURCES = ("decode.hip", "pkv_device.hpp", "pkv_internal.hpp")
 
 
+def verify_balanced(w) -> bool:
+    """Which kernels paged_attn_spec_verify runs for this batch (for the report only; the library decides):
+    the balanced split when a bf16 cache at head dim 128 gives each wave 4 or 8 query heads whose rows fit 32
+    matrix-core columns, over at least 128 (sequence, kv head, head subgroup) streams."""
+    g = w.num_q_heads // w.num_kv_heads
+    gb = 8 if g % 8 == 0 else 4 if g % 4 == 0 else 0
+    rows = w.q_chunk.shape[1]
+    return (w.dtype == "bf16" and w.head_dim == 128 and gb > 0 and gb * rows <= 32
+            and w.num_chunks * w.num_q_heads // gb >= 128)
+
+
 def sources_sha256() -> str:
     """Hash of the sources the decode kernels are built from."""
     h = hashlib.sha256()
@@ -339,7 +350,9 @@ def main():
         work, unit, peak, bound = dec["total"], "GB/s", HBM_PEAK_GBS, "hbm"
         rate = lambda ms: dec["total"] / (ms * 1e-3) / 1e9  # noqa: E731
     kernel = ("paged_attn_prefill_chunk_ws: prefill_mfma_kernel<chunk>" if prefill_only else
-              "paged_attn_spec_verify: prefill_mfma_kernel<split> + prefill_split_merge_kernel" if verify else
+              ("paged_attn_spec_verify: decode_balanced_kernel<verify rows> + decode_balanced_merge_kernel"
+               if verify_balanced(w) else
+               "paged_attn_spec_verify: prefill_mfma_kernel<split> + prefill_split_merge_kernel") if verify else
               ("paged_attn_decode_shared_prefix: prefill_mfma_kernel<prefix> + prefix_merge_kernel + "
                "decode_balanced_kernel + decode_balanced_merge_kernel") if cascade else
               ("paged_attn_decode_fp8: decode_balanced_kernel<fp8> + decode_balanced_merge_kernel"
@@ -372,7 +385,9 @@ def main():
                    "context_tokens": int((w.chunk_context_lens if verify else w.context_lens).sum()),
                    "max_context_len": w.max_context_len,
                    "split": "one workgroup per (chunk, kv head, 128-row tile)" if prefill_only else
-                            ("keys of each (sequence, kv head) cut into pieces" if w.num_chunks * w.num_kv_heads < 256
+                            ("balanced over 1024 wavefronts, heads x rows of a (sequence, kv head) as matrix-core "
+                             "columns" if verify_balanced(w) else
+                             "keys of each (sequence, kv head) cut into pieces" if w.num_chunks * w.num_kv_heads < 256
                              else "one workgroup per (sequence, kv head)") if verify else
                             f"fixed partitions of {part} tokens" if part else
                             (f"shared prefix of {len(w.shared_blocks) * 16} tokens attended once, then " if cascade

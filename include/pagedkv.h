@@ -400,11 +400,18 @@ int paged_attn_prefill_chunk_ws(const void* q_chunk, int32_t num_chunks, int32_t
  * i at position row_start[s] + i attends causally to keys 0 .. that position:
  * exactly paged_attn_prefill_chunk's result with chunk_len_max = rows_max
  * (same argument layout and device-side contract, rows past a sequence's
- * count not written), computed as by paged_attn_prefill_chunk_ws: the rows of
- * a sequence are few, so they share one row tile per kv head, and with few
- * sequences each (sequence, kv head)'s keys are cut into pieces spread over
- * the GPU.  Workspace: at least paged_attn_spec_verify_workspace_bytes(...)
- * bytes, 16-byte aligned (0: none needed).
+ * count not written).  Two work splits.  With a bf16 cache at head_dim 128,
+ * four or eight query heads per wavefront (num_q_heads / num_kv_heads a
+ * multiple of 4) whose rows fit 32 matrix-core columns (heads per wavefront x
+ * rows_max <= 32), and at least 128 (sequence, kv head, head subgroup)
+ * streams: the decode's balanced split, each stream's heads x rows the
+ * columns of its score and value products, every row masked at its own
+ * position, its blocks cut over 1024 wavefronts by cost and the cut streams
+ * merged.  Otherwise as paged_attn_prefill_chunk_ws: the rows of a sequence
+ * share one row tile per kv head, and with few sequences each (sequence, kv
+ * head)'s keys are cut into pieces spread over the GPU.  Workspace: at least
+ * paged_attn_spec_verify_workspace_bytes(...) bytes, 16-byte aligned (0: none
+ * needed; the size covers a bf16 cache, which the balanced split needs).
  */
 size_t paged_attn_spec_verify_workspace_bytes(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq);

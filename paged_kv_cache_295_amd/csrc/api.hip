@@ -611,8 +611,18 @@ int paged_attn_prefill_chunk_ws(const void* q_chunk, int32_t num_chunks, int32_t
 
 size_t paged_attn_spec_verify_workspace_bytes(int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
-  return paged_attn_prefill_chunk_workspace_bytes(num_seqs, rows_max, num_q_heads, num_kv_heads, head_dim,
-                                                  max_blocks_per_seq);
+  const size_t chunk = paged_attn_prefill_chunk_workspace_bytes(num_seqs, rows_max, num_q_heads, num_kv_heads,
+                                                                head_dim, max_blocks_per_seq);
+  if (chunk == 0 && (num_seqs <= 0 || rows_max <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+                     max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0))
+    return 0;
+  // the balanced split's partial slots where a bf16 cache of this shape takes it
+  const int gb = heads_per_wave(num_q_heads / num_kv_heads);
+  const size_t bal =
+      verify_takes_balanced(num_seqs, rows_max, num_q_heads, num_kv_heads, head_dim, PKV_DTYPE_BF16)
+          ? verify_workspace(gb, head_dim, rows_max)
+          : 0;
+  return chunk > bal ? chunk : bal;
 }
 
 int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, int32_t num_q_heads,
@@ -620,9 +630,43 @@ int paged_attn_spec_verify(const void* q, int32_t num_seqs, int32_t rows_max, in
                            const pkv_cache_desc* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, float scale, void* out, void* workspace,
                            size_t workspace_bytes, void* hip_stream) {
-  return paged_attn_prefill_chunk_ws(q, num_seqs, rows_max, num_q_heads, row_start, k_cache, v_cache, cache,
-                                     block_tables, max_blocks_per_seq, context_lens, scale, out, workspace,
-                                     workspace_bytes, hip_stream);
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !row_start || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (rows_max <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE >= (int64_t)1 << 31) return PKV_ERR_SHAPE;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  const int gb = heads_per_wave(num_q_heads / cache->num_kv_heads);
+  if (!verify_takes_balanced(num_seqs, rows_max, num_q_heads, cache->num_kv_heads, cache->head_dim, cache->dtype))
+    return paged_attn_prefill_chunk_ws(q, num_seqs, rows_max, num_q_heads, row_start, k_cache, v_cache, cache,
+                                       block_tables, max_blocks_per_seq, context_lens, scale, out, workspace,
+                                       workspace_bytes, hip_stream);
+  const size_t need = verify_workspace(gb, cache->head_dim, rows_max);
+  if (!workspace_ok(workspace, workspace_bytes, need)) return PKV_ERR_WORKSPACE;
+  DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.chunk_start = row_start;
+  a.num_seqs = num_seqs;
+  a.rows_per_seq = rows_max;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.dtype = cache->dtype;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale_log2 = scale * kLog2eHost;
+  a.balanced_waves = kVerifyWaves;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)kVerifyWaves * 2 * (gb * rows_max <= 16 ? 16 : 32) * cache->head_dim;
+  return from_hip(launch_verify(a, as_stream(hip_stream)));
 }
 
 }  // extern "C"

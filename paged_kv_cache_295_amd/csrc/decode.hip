@@ -244,7 +244,7 @@ constexpr float kRescaleSlack = 8.0f;
 // One wave's attention state for GB query heads of one kv head over a run of
 // consecutive blocks of one sequence (a "segment"): the query chunks, and per
 // token group the running max m (log2 units), sum l and unnormalised output.
-template <typename KV, int D, int GB, int LPT, int NS>
+template <typename KV, int D, int GB, int LPT, int NS, int CT = 1>
 struct Segment {
   using S = DecodeShape<KV, D, GB, LPT>;
   using E = typename S::E;
@@ -272,18 +272,26 @@ struct Segment {
   // and lane i receives dim i of tokens 4 g .. 4 g + 3); the copy's 8-byte
   // units are XOR-swizzled by token so that those reads hit distinct banks.
   // No partial dot products, no score reductions, no token groups to merge.
+  // Columns: with several query rows per sequence (the rows that verify draft
+  // tokens), column c = 16 ct + n of column tile ct is row c / GB, head c % GB
+  // of the group, with its own causal end; CT tiles share the K chunks of the
+  // score products and the V^T reads of the value products.
   static constexpr bool kMfma =
       (std::is_same<KV, Fp8E4M3>::value || (std::is_same<KV, __bf16>::value && NS >= PKV_DECODE_MFMA_BF16_MIN_STAGES)) &&
       D == 128 && (GB == 4 || GB == 8);
   static constexpr int kKC = RB / 64;  // K chunks per lane per block
   static_assert(!kMfma || (BPT == 1 && NP * CPL == kKC && TPP * NP == kBlock), "one block per tile");
+  static_assert(CT == 1 || kMfma, "column tiles are a matrix-core segment layout");
   // scales carried per stage (one dummy entry when there are none)
   static constexpr int NSC = kScaled ? (kMfma ? 4 : NP) : 1;
 
   Chunk qv[GB][CPL][QPC];
-  bf16x8_t qa[4];        // matrix-core segment: Q^T, the B operand of the four score products
-  float mh, lh;          // matrix-core segment: running max / sum of head lane % 16 (this lane's tokens)
-  f32x4_t oacc[D / 16];  // matrix-core segment: O^T, lane l: head l % 16, dims 16 t + 4 (l / 16) + i
+  // matrix-core segment, per column tile ct (lane l holds column 16 ct + l % 16):
+  bf16x8_t qa[CT][4];        // Q^T, the B operand of the four score products
+  float mh[CT], lh[CT];      // running max / sum of the column (this lane's tokens)
+  f32x4_t oacc[CT][D / 16];  // O^T, dims 16 t + 4 (l / 16) + i of the column
+  int ckeys[CT];             // keys the column attends to (0: no such column)
+  int cols;                  // columns in use: GB times the rows
   float m[GB], l[GB], acc[GB][CPL][EPC];
   bool bad_block;
   int tg, li;
@@ -308,17 +316,27 @@ struct Segment {
     sl2 = a.scale_log2;
   }
 
-  // The chunks of the GB query rows at qrow (head h0 of the row) this lane multiplies.
-  __device__ __forceinline__ void load_q(const T* __restrict__ qrow) {
+  // The chunks of the GB query rows at qrow (head h0 of the row) this lane
+  // multiplies.  Matrix-core segment: nrows rows rstride elements apart, row r
+  // attending to keys [0, min(end, key0 + r)).
+  __device__ __forceinline__ void load_q(const T* __restrict__ qrow, int64_t rstride, int nrows, int key0, int end) {
     if constexpr (kMfma) {
       const int lane = __lane_id();
       const int hm = lane & 15, q = lane >> 4;
+      cols = GB * nrows;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // the dims product i takes from lane group q (bf16: chunk i; E4M3: half i % 2 of chunk i / 2)
-        const int dim = std::is_same<KV, __bf16>::value ? 32 * i + 8 * q : 64 * (i >> 1) + 16 * q + 8 * (i & 1);
-        const Chunk c = hm < GB ? load_chunk(qrow + hm * D + dim) : Chunk{};
-        qa[i] = as_bf16x8(c.w[0], c.w[1], c.w[2], c.w[3]);
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c = 16 * ct + hm, r = c / GB, h = c % GB;
+        const bool live = c < cols;
+        ckeys[ct] = live ? min(end, key0 + r) : 0;
+        const T* qc = qrow + r * rstride + h * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // the dims product i takes from lane group q (bf16: chunk i; E4M3: half i % 2 of chunk i / 2)
+          const int dim = std::is_same<KV, __bf16>::value ? 32 * i + 8 * q : 64 * (i >> 1) + 16 * q + 8 * (i & 1);
+          const Chunk ch = live ? load_chunk(qc + dim) : Chunk{};
+          qa[ct][i] = as_bf16x8(ch.w[0], ch.w[1], ch.w[2], ch.w[3]);
+        }
       }
       return;
     }
@@ -344,10 +362,13 @@ struct Segment {
     }
     bad_block = false;
     if constexpr (kMfma) {
-      mh = kMaxInit;
-      lh = 0.0f;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) oacc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ct = 0; ct < CT; ++ct) {
+        mh[ct] = kMaxInit;
+        lh[ct] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) oacc[ct][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
     }
   }
 
@@ -418,7 +439,7 @@ struct Segment {
   __device__ __forceinline__ void compute(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
                                           const float (&sk)[NSC], const float (&sv)[NSC], int tok0, int end) {
     if constexpr (kMfma) {
-      compute_mfma(kk, vv, sk, sv, tok0 - tg, end);
+      compute_mfma(kk, vv, sk, sv, tok0 - tg);
       return;
     }
     float x[NP * GB];
@@ -490,7 +511,7 @@ struct Segment {
 
   // The matrix-core segment's block (tile = one block; its first token blk_tok).
   __device__ __forceinline__ void compute_mfma(const Chunk (&kk)[NP][CPL], const Chunk (&vv)[NP][CPL],
-                                               const float (&sk)[NSC], const float (&sv)[NSC], int blk_tok, int end) {
+                                               const float (&sk)[NSC], const float (&sv)[NSC], int blk_tok) {
     typedef short s16x4_t __attribute__((ext_vector_type(4)));
     // one 16-token x 128-dim bf16 V tile per wave (the workgroup is the wave)
     __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kBlock * D];
@@ -523,8 +544,10 @@ struct Segment {
       }
     }
 
-    // scores S[token 4 g + i][head n]
-    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+    // scores S[token 4 g + i][column n] of each column tile
+    f32x4_t d[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) d[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x8_t a;
@@ -537,36 +560,41 @@ struct Segment {
         a = as_bf16x8(fp8x2_to_bf16x2<false>(c.w[w]), fp8x2_to_bf16x2<true>(c.w[w]),
                       fp8x2_to_bf16x2<false>(c.w[w + 1]), fp8x2_to_bf16x2<true>(c.w[w + 1]));
       }
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qa[i], d, 0, 0, 0);
-    }
-    float s[4], bm = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool live = n < GB && blk_tok + 4 * g + i < end;
-      s[i] = live ? d[i] * (kScaled ? sk[kScaled ? i : 0] * sl2 : sl2) : -__builtin_inff();
-      bm = fmaxf(bm, s[i]);
+      for (int ct = 0; ct < CT; ++ct) d[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qa[ct][i], d[ct], 0, 0, 0);
     }
-    bm = xor_max<32>(xor_max<16>(bm));  // the block max of head n, in all four lane groups
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bm > mh + kRescaleSlack) != 0, 0)) {
-      const float mn = fmaxf(mh, bm);
-      const float alpha = fast_exp2(mh - mn);
-      mh = mn;
-      lh *= alpha;
+    s16x4_t pt[CT];
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) oacc[t] *= alpha;
-    }
-    float pv[4];
+    for (int ct = 0; ct < CT; ++ct) {
+      float s[4], bm = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pr = fast_exp2(s[i] - mh);  // 0 for a masked token or a padding head
-      lh += pr;
-      // scaled caches: the token's V scale joins the weight (the sum keeps the plain one)
-      pv[i] = kScaled ? (s[i] > -__builtin_inff() ? pr * sv[kScaled ? i : 0] : 0.0f) : pr;
+      for (int i = 0; i < 4; ++i) {
+        const bool live = blk_tok + 4 * g + i < ckeys[ct];  // never for a column not in use
+        s[i] = live ? d[ct][i] * (kScaled ? sk[kScaled ? i : 0] * sl2 : sl2) : -__builtin_inff();
+        bm = fmaxf(bm, s[i]);
+      }
+      bm = xor_max<32>(xor_max<16>(bm));  // the block max of column n, in all four lane groups
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(bm > mh[ct] + kRescaleSlack) != 0, 0)) {
+        const float mn = fmaxf(mh[ct], bm);
+        const float alpha = fast_exp2(mh[ct] - mn);
+        mh[ct] = mn;
+        lh[ct] *= alpha;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) oacc[ct][t] *= alpha;
+      }
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pr = fast_exp2(s[i] - mh[ct]);  // 0 for a masked token or an unused column
+        lh[ct] += pr;
+        // scaled caches: the token's V scale joins the weight (the sum keeps the plain one)
+        pv[i] = kScaled ? (s[i] > -__builtin_inff() ? pr * sv[kScaled ? i : 0] : 0.0f) : pr;
+      }
+      const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
+      pt[ct] = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
     }
-    const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
-    const s16x4_t pt = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
 
-    // O^T[16 t .. 16 t + 15][head] += V^T P^T
+    // O^T[16 t .. 16 t + 15][column] += V^T P^T (one V^T read serves every column tile)
     const int tt = 4 * g + (n >> 2);  // the token this lane addresses for the transposing reads
     const char* rrow = reinterpret_cast<const char*>(vt_lds) + tt * (D * 2);
 #pragma unroll
@@ -574,7 +602,9 @@ struct Segment {
       const int u = 4 * t + (n & 3);
       const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4_t*)(rrow + (u ^ swz(tt)) * 8));
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, oacc[t], 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        oacc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt[ct], oacc[ct][t], 0, 0, 0);
     }
   }
 
@@ -636,11 +666,14 @@ struct Segment {
   // Attend the GB query rows at qrow (head h0 of the row) over tokens
   // [16 * blk0, end) of one sequence, whose blocks blk0 .. blk0 + nblk - 1 are
   // listed at table[0 .. nblk - 1], for kv head g; seed_row >= 0 starts from
-  // the shared-prefix state of that row (see seed).
+  // the shared-prefix state of that row (see seed).  Matrix-core segment with
+  // several rows: nrows rows rstride elements apart, row r seeing the keys
+  // before min(end, key0 + r).
   __device__ __forceinline__ void run(const DecodeArgs& a, const T* __restrict__ qrow,
                                       const int32_t* __restrict__ table, int g, int blk0, int nblk, int end,
-                                      int64_t seed_row = -1) {
-    load_q(qrow);
+                                      int64_t seed_row = -1, int64_t rstride = 0, int nrows = 1,
+                                      int key0 = 0x7fffffff) {
+    load_q(qrow, rstride, nrows, key0, end);
     reset();
     if (seed_row >= 0) {
       // The shared-prefix call runs the two-stage vector-ALU segment, which
@@ -780,8 +813,9 @@ struct Segment {
   __device__ __forceinline__ void merge_groups() {
     static_assert(LPT == 4 || LPT == 8 || LPT == 16, "token groups differ in lane bits 2..5, 3..5 or 4..5");
     bad_block = __builtin_amdgcn_ballot_w64(bad_block) != 0;
-    if constexpr (kMfma) {  // one running max per head already; the sums of the four lane groups
-      lh = xor_add<32>(xor_add<16>(lh));
+    if constexpr (kMfma) {  // one running max per column already; the sums of the four lane groups
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) lh[ct] = xor_add<32>(xor_add<16>(lh[ct]));
       return;
     }
 #pragma unroll
@@ -813,18 +847,24 @@ struct Segment {
     const int c = (v / EPC) % CPL, e = v % EPC;
     return head * D + (c * LPT + li) * EPC + e;
   }
-  // Normalised output of the GB heads at outp (head h0 of the row).
-  __device__ __forceinline__ void store_out(T* __restrict__ outp) {
+  // Normalised output of the GB heads at outp (head h0 of the row; matrix-core
+  // segment: row r of the columns at outp + r * rstride).
+  __device__ __forceinline__ void store_out(T* __restrict__ outp, int64_t rstride = 0) {
     const float nan = __builtin_nanf("");
-    if constexpr (kMfma) {  // lane 16 g + n (n < GB): dims 16 t + 4 g .. + 3 of head n
+    if constexpr (kMfma) {  // lane 16 g + n: dims 16 t + 4 g .. + 3 of column 16 ct + n
       const int lane = __lane_id();
       const int n = lane & 15, g = lane >> 4;
-      if (n < GB) {
-        const float inv = bad_block ? nan : 1.0f / lh;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c = 16 * ct + n, r = c / GB, h = c % GB;
+        if (c >= cols) continue;
+        const float inv = bad_block ? nan : 1.0f / lh[ct];
+        T* o = outp + r * rstride + h * D;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-          *reinterpret_cast<uint2*>(outp + n * D + 16 * t + 4 * g) =
-              make_uint2(pack_bf16x2(oacc[t][0] * inv, oacc[t][1] * inv), pack_bf16x2(oacc[t][2] * inv, oacc[t][3] * inv));
+          *reinterpret_cast<uint2*>(o + 16 * t + 4 * g) =
+              make_uint2(pack_bf16x2(oacc[ct][t][0] * inv, oacc[ct][t][1] * inv),
+                         pack_bf16x2(oacc[ct][t][2] * inv, oacc[ct][t][3] * inv));
       }
       return;
     }
@@ -871,22 +911,25 @@ struct Segment {
     }
   }
 
-  // Partial (m, l, unnormalised o) of head h at po + h * ostride (D floats) and
-  // pml + h * mlstride (2 floats).
+  // Partial (m, l, unnormalised o) of head h (matrix-core segment: column h)
+  // at po + h * ostride (D floats) and pml + h * mlstride (2 floats).
   __device__ __forceinline__ void store_partial(float* __restrict__ po, int64_t ostride, float* __restrict__ pml,
                                                 int64_t mlstride) {
     const float nan = __builtin_nanf("");
     if constexpr (kMfma) {
       const int lane = __lane_id();
       const int n = lane & 15, g = lane >> 4;
-      if (n < GB) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c = 16 * ct + n;
+        if (c >= cols) continue;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-          *reinterpret_cast<float4*>(po + n * ostride + 16 * t + 4 * g) =
-              make_float4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3]);
+          *reinterpret_cast<float4*>(po + c * ostride + 16 * t + 4 * g) =
+              make_float4(oacc[ct][t][0], oacc[ct][t][1], oacc[ct][t][2], oacc[ct][t][3]);
         if (g == 0) {
-          pml[n * mlstride] = bad_block ? nan : mh;
-          pml[n * mlstride + 1] = lh;
+          pml[c * mlstride] = bad_block ? nan : mh[ct];
+          pml[c * mlstride + 1] = lh[ct];
         }
       }
       return;
@@ -1079,6 +1122,21 @@ constexpr int kSegCost = PKV_SEGMENT_COST;
 
 __device__ __forceinline__ int seq_blocks(int L, int cap) { return (L >= 0 && L <= cap) ? (L + kBlock - 1) / kBlock : 0; }
 
+// Blocks a sequence's streams read.  Decode: its context.  The rows that
+// verify draft tokens (starts != nullptr, up to R rows from position
+// starts[s]): the keys of the last row, which are the whole context.  A
+// sequence outside its contract, or with no rows, reads nothing (the merge
+// kernel writes its NaN rows).
+template <bool VR>
+__device__ __forceinline__ int stream_blocks(int L, int P0, int cap, int R) {
+  if constexpr (VR) {
+    const int n = L - P0;
+    return (P0 >= 0 && n >= 1 && n <= R && L <= cap) ? (L + kBlock - 1) / kBlock : 0;
+  } else {
+    return seq_blocks(L, cap);
+  }
+}
+
 // Cost of all HH streams of a sequence with nb blocks.
 __device__ __forceinline__ int64_t seq_cost(int nb, int HH) { return nb > 0 ? (int64_t)HH * (nb + kSegCost) : 0; }
 
@@ -1115,14 +1173,16 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t x) {
 }
 
 // Total cost over all sequences, and the cost of the sequences before s
-// (every lane gets both); one pass over the lengths.
-__device__ __forceinline__ void cost_counts(const int32_t* __restrict__ lens, int B, int s, int cap, int HH,
-                                            int64_t& total, int64_t& before) {
+// (every lane gets both); one pass over the lengths (and row starts).
+template <bool VR>
+__device__ __forceinline__ void cost_counts(const int32_t* __restrict__ lens, const int32_t* __restrict__ starts,
+                                            int B, int s, int cap, int R, int HH, int64_t& total, int64_t& before) {
   total = 0;
   before = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int i = c0 + __lane_id();
-    const int64_t incl = wave_incl_scan(i < B ? seq_cost(seq_blocks(lens[i], cap), HH) : 0);
+    const int64_t incl =
+        wave_incl_scan(i < B ? seq_cost(stream_blocks<VR>(lens[i], VR ? starts[i] : 0, cap, R), HH) : 0);
     const int64_t all = readlane64(incl, kWave - 1);
     total += all;
     if (s >= c0 + kWave) {
@@ -1152,10 +1212,16 @@ __device__ __forceinline__ int64_t range_begin(int w, int W, int64_t U) { return
 // The wave whose range holds cost unit u.
 __device__ __forceinline__ int wave_of(int64_t u, int W, int64_t U) { return (int)(((u + 1) * W + U - 1) / U) - 1; }
 
-template <typename KV, int D, int GB, int LPT, int NS>
+// VR: the rows that verify draft tokens (a.chunk_start: first row position
+// per sequence, a.rows_per_seq rows at most), row r of a sequence seeing the
+// keys before a.chunk_start[s] + r + 1; a stream's GB heads x rows are the
+// columns of CT matrix-core column tiles, and a partial slot holds 16 CT
+// columns.  Otherwise a decode (one row).
+template <typename KV, int D, int GB, int LPT, int NS, int CT = 1, bool VR = false>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
                                                               const int32_t* __restrict__ lens) {
   using T = typename KvTraits<KV>::Q;
+  constexpr int kSlotCols = VR ? 16 * CT : GB;  // columns of a partial slot
   const int lane = __lane_id();
   const int W = gridDim.x;
   const int w = blockIdx.x;
@@ -1164,6 +1230,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
   const int hsubs = G / GB;
   const int HH = a.num_kv_heads * hsubs;  // streams per sequence
   const int cap = a.max_blocks_per_seq * kBlock;
+  const int R = VR ? a.rows_per_seq : 1;
+  const int32_t* __restrict__ starts = a.chunk_start;
 
   // A batch of at most 64 sequences keeps every length in a lane: one load
   // gives the total cost, this wave's first sequence and every later length
@@ -1171,13 +1239,14 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
   // next sequence needs none).
   const bool small = B <= kWave;
   const int Llane = small && lane < B ? lens[lane] : 0;
+  const int Plane = VR && small && lane < B ? starts[lane] : 0;
   int64_t U;
   int s = 0;
   int64_t cum = 0;
-  int L;
+  int L, P0 = 0;
   int64_t u0, u1;
   if (small) {
-    const int64_t c = lane < B ? seq_cost(seq_blocks(Llane, cap), HH) : 0;
+    const int64_t c = lane < B ? seq_cost(stream_blocks<VR>(Llane, Plane, cap, R), HH) : 0;
     const int64_t incl = wave_incl_scan(c);
     U = uniform64(readlane64(incl, kWave - 1));
     u0 = range_begin(w, W, U);
@@ -1188,16 +1257,17 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
     s = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
     cum = uniform64(readlane64(incl - c, s));
     L = __builtin_amdgcn_readlane(Llane, s);
+    if constexpr (VR) P0 = __builtin_amdgcn_readlane(Plane, s);
   } else {
     int64_t unused;
-    cost_counts(lens, B, 0, cap, HH, U, unused);
+    cost_counts<VR>(lens, starts, B, 0, cap, R, HH, U, unused);
     u0 = range_begin(w, W, U);
     u1 = range_begin(w + 1, W, U);
     if (u0 >= u1) return;
     // locate u0: the sequence s whose cost interval [cum, cum + cost) holds it
     for (int c0 = 0; c0 < B; c0 += kWave) {
       const int i = c0 + lane;
-      const int64_t c = i < B ? seq_cost(seq_blocks(lens[i], cap), HH) : 0;
+      const int64_t c = i < B ? seq_cost(stream_blocks<VR>(lens[i], VR ? starts[i] : 0, cap, R), HH) : 0;
       const int64_t incl = wave_incl_scan(c);
       const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && cum + incl > u0);
       if (hit) {
@@ -1211,10 +1281,11 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
     s = __builtin_amdgcn_readfirstlane(s);
     cum = uniform64(cum);
     L = lens[s];
+    if constexpr (VR) P0 = starts[s];
   }
 
-  Segment<KV, D, GB, LPT, NS> seg(a);
-  int nb = seq_blocks(L, cap);
+  Segment<KV, D, GB, LPT, NS, CT> seg(a);
+  int nb = stream_blocks<VR>(L, P0, cap, R);
   bool first = true;
   for (int64_t u = u0;;) {
     const int64_t span = nb + kSegCost;  // cost of one stream of sequence s
@@ -1226,15 +1297,21 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
     const int j = (int)(ub - sb), jn = (int)(seg_end - sb);
     const int g = k / hsubs, hs = k - g * hsubs;
     const int h0 = g * G + hs * GB;
-    const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)s * a.num_q_heads + h0) * D;
-    seg.run(a, qrow, tables + (int64_t)s * a.max_blocks_per_seq + j, g, j, jn - j, min(L, jn * kBlock),
-            (a.init_o != nullptr && j == 0) ? (int64_t)s * a.num_q_heads + h0 : -1);
+    const int64_t row0 = ((int64_t)s * R * a.num_q_heads + h0) * D;  // head h0 of the sequence's first row
+    const int64_t rstride = (int64_t)a.num_q_heads * D;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + row0;
+    const int32_t* tab = tables + (int64_t)s * a.max_blocks_per_seq + j;
+    if constexpr (VR)
+      seg.run(a, qrow, tab, g, j, jn - j, min(L, jn * kBlock), -1, rstride, L - P0, P0 + 1);
+    else
+      seg.run(a, qrow, tab, g, j, jn - j, min(L, jn * kBlock),
+              (a.init_o != nullptr && j == 0) ? (int64_t)s * a.num_q_heads + h0 : -1);
     seg.merge_groups();
     if (j == 0 && jn == nb) {
-      seg.store_out(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + h0) * D);
+      seg.store_out(reinterpret_cast<T*>(a.out) + row0, rstride);
     } else {
       const int64_t slot = (int64_t)w * 2 + (first ? 0 : 1);
-      seg.store_partial(a.part_o + slot * GB * D, D, a.part_ml + slot * GB * 2, 2);
+      seg.store_partial(a.part_o + slot * kSlotCols * D, D, a.part_ml + slot * kSlotCols * 2, 2);
     }
     first = false;
     u = seg_end;
@@ -1244,7 +1321,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
       do {
         ++s;
         L = small ? __builtin_amdgcn_readlane(Llane, s) : lens[s];
-        nb = seq_blocks(L, cap);
+        if constexpr (VR) P0 = small ? __builtin_amdgcn_readlane(Plane, s) : starts[s];
+        nb = stream_blocks<VR>(L, P0, cap, R);
       } while (nb == 0);
     }
   }
@@ -1263,7 +1341,12 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(const DecodeArgs a,
 // per wave; with many streams every wave repeats the cost scan over the
 // lengths, and the whole group per wave is faster (the 256-sequence batch,
 // 2048 streams: the call took 104 us with one head per wave against 100 us).
-template <typename T, int D, int GB, int HM>
+//
+// VR (the rows that verify draft tokens): one wave per (sequence, stream,
+// row, HM heads), the partial columns of row r being r GB .. r GB + GB - 1; a
+// partial slot holds SC columns.  A sequence outside its contract gets NaN in
+// all its rows; rows past its count are not written.
+template <typename T, int D, int GB, int HM, bool VR = false, int SC = GB>
 __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeArgs a, int W) {
   constexpr int PER = D / kWave;
   constexpr int kPre = HM == 1 ? 16 : 4;
@@ -1274,16 +1357,30 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
   const int hsubs = G / GB;
   const int HH = a.num_kv_heads * hsubs;
   const int cap = a.max_blocks_per_seq * kBlock;
-  const int hh0 = (blockIdx.x % (GB / HM)) * HM;  // first head of this wave within the stream's group
-  const int stream = blockIdx.x / (GB / HM);       // (sequence, stream)
+  const int R = VR ? a.rows_per_seq : 1;
+  const int CW = R * (GB / HM);  // waves per stream
+  const int cw = blockIdx.x % CW;
+  const int stream = blockIdx.x / CW;       // (sequence, stream)
+  const int r = cw / (GB / HM);             // row of the sequence (decode: 0)
+  const int hh0 = (cw % (GB / HM)) * HM;    // first head of this wave within the stream's group
+  const int pc0 = r * GB + hh0;             // its first column in a partial slot
   const int s = stream / HH;
   const int k = stream - s * HH;
   const int g = k / hsubs, hs = k - g * hsubs;
   const int head0 = g * G + hs * GB + hh0;
-  T* outp = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_q_heads + head0) * D;
+  T* outp = reinterpret_cast<T*>(a.out) + (((int64_t)s * R + r) * a.num_q_heads + head0) * D;
 
   const int L = a.context_lens[s];
-  if (L == 0 && a.init_o != nullptr) {  // nothing after the shared prefix: its state alone
+  int P0 = 0;
+  if constexpr (VR) {
+    P0 = a.chunk_start[s];
+    const int n = L - P0;
+    if (P0 < 0 || n < 0 || n > R || L > cap) {
+      for (int i = lane; i < HM * D; i += kWave) outp[i] = (T)__builtin_nanf("");
+      return;
+    }
+    if (r >= n) return;  // no such row (or none at all)
+  } else if (L == 0 && a.init_o != nullptr) {  // nothing after the shared prefix: its state alone
     const int64_t split_stride = (int64_t)B * a.num_q_heads;
     const int64_t row0 = (int64_t)s * a.num_q_heads + head0;
     for (int h = 0; h < HM; ++h) {
@@ -1310,14 +1407,14 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
     }
     return;
   }
-  if (L < 0 || L > cap || L == 0) {
+  if (!VR && (L < 0 || L > cap || L == 0)) {
     const float fill = L == 0 ? 0.0f : __builtin_nanf("");
     for (int i = lane; i < HM * D; i += kWave) outp[i] = (T)fill;
     return;
   }
   int64_t U, before;
-  cost_counts(a.context_lens, B, s, cap, HH, U, before);
-  const int nb = seq_blocks(L, cap);
+  cost_counts<VR>(a.context_lens, a.chunk_start, B, s, cap, R, HH, U, before);
+  const int nb = stream_blocks<VR>(L, P0, cap, R);
   const int64_t as = before + (int64_t)k * (nb + kSegCost);  // the stream's cost interval starts here
   const int64_t us = as + kSegCost;                           // and its blocks here
   const int64_t ue = us + nb - 1;
@@ -1342,8 +1439,8 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
     float mc[HM], lc[HM];
 #pragma unroll
     for (int h = 0; h < HM; ++h) {
-      mc[h] = owner ? a.part_ml[(slot * GB + hh0 + h) * 2] : -__builtin_inff();
-      lc[h] = owner ? a.part_ml[(slot * GB + hh0 + h) * 2 + 1] : 0.0f;
+      mc[h] = owner ? a.part_ml[(slot * SC + pc0 + h) * 2] : -__builtin_inff();
+      lc[h] = owner ? a.part_ml[(slot * SC + pc0 + h) * 2 + 1] : 0.0f;
     }
     // the outputs of the first kPre candidates do not depend on the (m, l)
     // values: their loads go out together with them
@@ -1358,7 +1455,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
       for (int h = 0; h < HM; ++h)
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-          opre[j][h][e] = oj ? a.part_o[(sj * GB + hh0 + h) * D + lane + e * kWave] : 0.0f;
+          opre[j][h][e] = oj ? a.part_o[(sj * SC + pc0 + h) * D + lane + e * kWave] : 0.0f;
     }
     float f[HM];
 #pragma unroll
@@ -1392,7 +1489,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const DecodeA
         const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f[h]), j));
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-          o[h][e] = fmaf(fj, a.part_o[(sj * GB + hh0 + h) * D + lane + e * kWave], o[h][e]);
+          o[h][e] = fmaf(fj, a.part_o[(sj * SC + pc0 + h) * D + lane + e * kWave], o[h][e]);
       }
     }
   }
@@ -1670,6 +1767,45 @@ static hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
     case 8: return launch_typed<KV, D, 8>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// The rows that verify draft tokens, on the balanced split with the
+// matrix-core segment: GB heads x rows_per_seq rows are the columns of CT
+// column tiles.
+template <int GB, int CT>
+static hipError_t launch_verify_cols(const DecodeArgs& a, hipStream_t stream) {
+  using KV = __bf16;
+  constexpr int D = 128;
+  constexpr int NS = deep_stages<KV, D, GB>();
+  constexpr int LPT = lanes_per_token<KV, D, GB>();
+  static_assert(Segment<KV, D, GB, LPT, NS, CT>::kMfma, "verify rows take the matrix-core segment");
+  const int hsubs = (a.num_q_heads / a.num_kv_heads) / GB;
+  const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads * hsubs * a.rows_per_seq;  // (stream, row) pairs
+  if (rows * GB > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_balanced_kernel<KV, D, GB, LPT, NS, CT, true>), dim3(a.balanced_waves), dim3(64), 0,
+                     stream, a, a.block_tables, a.context_lens);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // one head per merge wave while that keeps the grid small, as for decode
+  // (measured on 16..64 sequences x 5 rows: 37.5 against 40.7 us at 16
+  // sequences, 82.3 against 79.3 us at 48)
+  if (rows * GB <= kMergeWavesPerHead)
+    hipLaunchKernelGGL((decode_balanced_merge_kernel<__bf16, D, GB, 1, true, 16 * CT>), dim3((unsigned)(rows * GB)),
+                       dim3(64), 0, stream, a, a.balanced_waves);
+  else
+    hipLaunchKernelGGL((decode_balanced_merge_kernel<__bf16, D, GB, GB, true, 16 * CT>), dim3((unsigned)rows),
+                       dim3(64), 0, stream, a, a.balanced_waves);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const DecodeArgs& a, hipStream_t stream) {
+  const int gb = heads_per_wave(a.num_q_heads / a.num_kv_heads);
+  if (!verify_balanced(gb, a.dtype, a.head_dim, a.rows_per_seq) || a.chunk_start == nullptr ||
+      a.balanced_waves <= 0)
+    return hipErrorInvalidValue;
+  const bool one = gb * a.rows_per_seq <= 16;
+  if (gb == 4) return one ? launch_verify_cols<4, 1>(a, stream) : launch_verify_cols<4, 2>(a, stream);
+  return one ? launch_verify_cols<8, 1>(a, stream) : launch_verify_cols<8, 2>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -163,4 +163,33 @@ constexpr int balanced_waves_max(int gb) {
   return w;
 }
 
+// The rows that verify draft tokens run on the balanced split with the
+// matrix-core segment where its columns (heads per wave x rows) fit two column
+// tiles -- bf16 caches, D = 128, four or eight heads per wave -- and the batch
+// has at least kVerifyMinStreams (sequence, kv head, head subgroup) streams,
+// over kVerifyWaves waves, each leaving at most two partial slots of 16 or 32
+// columns.  Fewer streams keep the matrix-core chunk kernel with its key
+// split: their keys are cut into so many pieces over the 1024 waves that the
+// partials of 20 columns per piece cost more than the split saves (5 rows x
+// 32q / 8kv heads, contexts U{128..4096}, cold caches: 8 sequences 29.5 us
+// against 26.1 on the chunk kernel; 16 sequences 37.5 against 52.1; 32: 55.9
+// against 73.0; 64: 99.8 against 107.1; 128: 200.3 against 203.2).
+constexpr int kVerifyWaves = 1024;
+constexpr int64_t kVerifyMinStreams = 128;
+constexpr bool verify_balanced(int gb, int dtype, int head_dim, int rows) {
+  return dtype == 1 && head_dim == 128 && (gb == 4 || gb == 8) && rows >= 1 && gb * rows <= 32;
+}
+constexpr bool verify_takes_balanced(int64_t num_seqs, int rows, int num_q_heads, int num_kv_heads, int head_dim,
+                                     int dtype) {
+  return num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+         verify_balanced(heads_per_wave(num_q_heads / num_kv_heads), dtype, head_dim, rows) &&
+         num_seqs * num_q_heads / heads_per_wave(num_q_heads / num_kv_heads) >= kVerifyMinStreams;
+}
+constexpr size_t verify_workspace(int gb, int head_dim, int rows) {
+  return (size_t)kVerifyWaves * 2 * (gb * rows <= 16 ? 16 : 32) * ((size_t)head_dim + 2) * sizeof(float);
+}
+// a.chunk_start: each sequence's first row position; a.rows_per_seq rows at
+// most; a.part_o / a.part_ml: the partial slots (kVerifyWaves of them).
+hipError_t launch_verify(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace pkv

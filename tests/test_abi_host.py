@@ -222,8 +222,19 @@ def test_spec_verify_validation_and_workspace(lib):
     assert v(hq=20) == SHAPE
     assert v(B=8, ws=None, wsb=0) == WS
     assert v(dd=desc(dt=2)) == DTYPE
-    # 64 sequences x 8 kv heads: a pair for every workgroup slot, no split and no workspace
-    assert lib.paged_attn_spec_verify_workspace_bytes(64, 5, 32, 8, 128, 257) == 0
+    # 64 sequences x 8 kv heads (512 streams of 4 heads x 5 rows = 20 columns): the balanced split over 1024
+    # waves, two partial slots of two 16-column tiles each
+    bal = lib.paged_attn_spec_verify_workspace_bytes(64, 5, 32, 8, 128, 257)
+    assert bal == 1024 * 2 * 32 * 130 * 4
+    assert v(wsb=bal - 1) == WS
+    # 4 rows of 4 heads fit one column tile; 16 sequences x 8 kv heads is the fewest streams that take it
+    assert lib.paged_attn_spec_verify_workspace_bytes(16, 4, 32, 8, 128, 257) == 1024 * 2 * 16 * 130 * 4
+    # 9 rows x 4 heads = 36 columns: the chunk kernel (no split with 64 sequences)
+    assert lib.paged_attn_spec_verify_workspace_bytes(64, 9, 32, 8, 128, 257) == 0
+    # 64 query heads per 8 kv heads: 8 heads x 4 rows = 32 columns
+    assert lib.paged_attn_spec_verify_workspace_bytes(64, 4, 64, 8, 128, 257) == 1024 * 2 * 32 * 130 * 4
+    # head dim 64 keeps the chunk kernel
+    assert lib.paged_attn_spec_verify_workspace_bytes(64, 5, 32, 8, 64, 257) == 0
     # 8 sequences x 8 kv heads of 5 rows, 257 blocks: 64 pairs for 512 workgroup slots, pieces
     # of ceil(64 * 4112 / 1024) = 257 -> 320 keys (whole tiles), 13 per row tile
     need = lib.paged_attn_spec_verify_workspace_bytes(8, 5, 32, 8, 128, 257)

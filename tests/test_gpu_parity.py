@@ -378,6 +378,40 @@ def test_spec_verify_bench_workloads(name):
     check_attn(got[:, :n], ref[:, :n], w.dtype, name)
 
 
+VERIFY_BALANCED_EDGES = [
+    # 16 sequences x 8 kv heads (128 streams, the fewest that take the balanced split), 4 heads x 5 rows in two
+    # column tiles, one head per merge wave: a sequence with no rows, empty accepted contexts, and one context
+    # of 30,000 tokens whose streams span more than 64 waves
+    ("g4-two-tiles", 32, 8, 5, [(0, 0), (0, 1), (15, 5), (16, 3), (30000, 5), (100, 0), (1, 2), (47, 4)], 8, 31),
+    # 64 query / 8 kv heads: 8 heads x 2 rows fill one column tile
+    ("g8-one-tile", 64, 8, 2, [(0, 1), (5, 0), (2047, 2), (33, 1)], 20, 32),
+]
+
+
+@pytest.mark.parametrize("case", VERIFY_BALANCED_EDGES, ids=lambda c: c[0])
+def test_spec_verify_balanced_edges(case):
+    """The verify call on the balanced split (bf16, head dim 128, heads x rows <= 32 columns): rows past a
+    sequence's count, and every row of a sequence with none, stay unwritten."""
+    _, hq, hkv, rows, fixed, n_random, seed = case
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pairs = fixed + [(int(rng.integers(1, 600)), int(rng.integers(1, rows + 1))) for _ in range(n_random)]
+    w = chunk_workload("bf16", hq, hkv, 128, pairs, seed=seed, cmax=rows)
+    dw = DeviceWorkload(w)
+    rk, rv = run_write(dw)
+    out, need = run_verify(dw)
+    gb = 8 if (hq // hkv) % 8 == 0 else 4
+    assert need == 1024 * 2 * (16 if gb * rows <= 16 else 32) * 130 * 4, "the balanced split's workspace"
+    say(f"{case[0]}: {w.num_chunks} sequences, workspace {need} bytes")
+    ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens, w.scale,
+                               w.dtype)
+    got = values(out)
+    for c in range(w.num_chunks):
+        n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+        if n:
+            check_attn(got[c, :n], ref[c, :n], w.dtype, f"balanced verify, sequence {c}")
+        assert (got[c, n:] == SENTINEL).all(), f"sequence {c}: rows past its count must not be written"
+
+
 def test_spec_verify_split_bad_sequence_gives_nan():
     """A sequence that breaks the contract (more rows than rows_max) gets NaN rows;
     the others are unaffected, with the keys split into pieces."""
