@@ -190,8 +190,15 @@ __device__ __forceinline__ void wait_vmcnt_le() {
 // output, the others write (m, l, o) partials for prefill_split_merge_kernel.
 constexpr int kChunk = 0, kPrefix = 1, kSplit = 2;
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_SIMD)))
+//
+// KH = 2 (key halves): a workgroup of two groups of four waves over the same
+// 128 rows, group kh taking key tiles kt0 + kh, kt0 + kh + 2, ... through its
+// own LDS ring (128 KiB per workgroup at head_dim 128), the two states of each
+// row merged through LDS at the end.  For grids of at most one workgroup per
+// compute unit it halves the chain of key tiles a row tile walks, at the same
+// waves per SIMD as two four-wave workgroups.
+template <int D, int MODE, int KH>
+__global__ __launch_bounds__(kThreads * KH) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_SIMD)))
 void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables) {
   constexpr bool PREFIX = MODE == kPrefix;
   using S = PrefillShape<D>;
@@ -199,12 +206,17 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   constexpr int RC = S::kRC;
   constexpr int RB = S::kRowBytes;
   constexpr int TB = S::kTileBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * S::kStageBytes];
-  const int smem_base = (int)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
+  static_assert(KH == 1 || KH == 2, "one or two key halves");
+  __shared__ __attribute__((aligned(1024))) char smem[KH * NS * S::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave_all / kWaves;  // key half of this wave
+  const int wave = wave_all - kh * kWaves;  // its place among the four waves of the half
+  const int htid = tid - kh * kThreads;  // thread index within the half
+  char* const hsm = smem + kh * NS * S::kStageBytes;  // the half's LDS ring
+  const int smem_base = (int)(uintptr_t)(const __attribute__((address_space(3))) void*)hsm;
   const int half = lane >> 5;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int id = blockIdx.x;
@@ -268,7 +280,7 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     if (bad_chunk) {
       if (sp != 0) return;  // piece 0 writes the NaN rows
       const int rows = min(QT, a.chunk_len_max - row0);
-      for (int idx = tid; idx < rows * G * D; idx += kThreads) {
+      for (int idx = tid; idx < rows * G * D; idx += kThreads * KH) {
         const int r = idx / (G * D), rem = idx - r * G * D;
         out[((int64_t)(c * a.chunk_len_max + row0 + r) * a.num_q_heads + g * G) * D + rem] =
             (__bf16)__builtin_nanf("");
@@ -355,8 +367,8 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   // prefix) keep the default policy: with the hint the large prefill took
   // 570 us against 542.
   const bool stream_kv = !PREFIX && a.chunk_len_max * G <= kMRows;
-  auto issue = [&](int kt, int p) {  // direct-to-LDS loads of this wave's rows of tile kt (block p)
-    char* kdst = smem + (kt % NS) * S::kStageBytes + wave * kRowsPerWave * RB;
+  auto issue = [&](int stage, int p) {  // direct-to-LDS loads of this wave's rows of a tile (block p)
+    char* kdst = hsm + stage * S::kStageBytes + wave * kRowsPerWave * RB;
     const int64_t boff = (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
     const char* kb = kc + boff;
     const char* vb = vc + boff;
@@ -508,56 +520,93 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
       }
   };
 
-  // V rows [r0, 64) of the tile at LDS address vt are past every row's keys:
-  // zero them (they may hold NaN), visible to every wave before they are read.
-  auto zero_tail = [&](int kt, char* vt) {
-    const int r0 = kend - kt * kKT;
-    if (r0 < kKT) {
-      for (int idx = tid; idx < (kKT - r0) * RC; idx += kThreads)
-        *reinterpret_cast<uint4*>(vt + (r0 + idx / RC) * RB + (idx % RC) * 16) = make_uint4(0u, 0u, 0u, 0u);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    }
-  };
-  // tiles with no key past any row's position, then the diagonal ones
+  // tiles with no key past any row's position come before the diagonal ones
   const int nfull = min(ntiles, mask_from / kKT);
+  // this half's tiles, kt0 + kh, kt0 + kh + KH, ...; both halves take the same
+  // number of steps (a step past the last tile only loads and synchronises)
+  const int nsteps = (ntiles - kt0 + KH - 1) / KH;
+  auto kt_of = [&](int i) { return kt0 + KH * i + kh; };
+  // The last tile also holds keys past every row's (unless kend is a multiple
+  // of the tile): its V rows from kend on are zeroed in LDS before they are
+  // read (they may hold NaN), at a step every wave of the workgroup takes.
+  const int kt_tail = kend % kKT ? ntiles - 1 : -1;
+  const int i_tail = kt_tail >= 0 ? (kt_tail - kt0) / KH : -1;
 
-  // prologue: tiles 0 .. NS-2 in flight (past the last tile: zero rows, so every
-  // iteration finds the same number of loads outstanding)
-  int pnext = table_entry(kt0);
+  // prologue: steps 0 .. NS-2 in flight (past the last tile: block 0, whose rows
+  // are never used, so every step finds the same number of loads outstanding)
+  int pnext = table_entry(kt_of(0));
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t) {
     const int p = pnext;
-    pnext = table_entry(kt0 + t + 1);
-    issue(kt0 + t, p);
+    pnext = table_entry(kt_of(t + 1));
+    issue(t, p);
   }
-  // Tile kt: wait for its loads, start the loads of tile kt + NS - 1, then
-  // S^T = K Q^T, the online softmax and O^T += V^T P^T (the last diagonal tile
-  // also holds keys past every row's, whose V rows are zeroed first).
-  auto tile = [&](auto mask_tag, int kt) {
-    // this wave's loads of tile kt are done once at most NS-2 tiles' loads remain;
-    // the barrier then makes every wave's part visible and frees the stage of kt-1
+  // Step i: wait for its tile's loads, start the loads of step i + NS - 1,
+  // then S^T = K Q^T, the online softmax and O^T += V^T P^T.  Two loops, the
+  // steps whose tile has no masked key, then the others: every step has the
+  // same barriers, so the halves stay in step whichever loop they are in.
+  auto step = [&](auto mask_tag, int i) {
+    // this wave's loads of step i are done once at most NS-2 steps' loads remain;
+    // the barrier then makes every wave's part visible and frees the stage of i-1
     wait_vmcnt_le<(NS - 2) * S::kDW>();
     __builtin_amdgcn_s_barrier();
     {
       const int p = pnext;
-      pnext = table_entry(kt + NS);
-      issue(kt + NS - 1, p);
+      pnext = table_entry(kt_of(i + NS));
+      issue((i + NS - 1) % NS, p);
     }
-    const int sbase = smem_base + (kt % NS) * S::kStageBytes;
-    if constexpr (decltype(mask_tag)::value) zero_tail(kt, smem + (kt % NS) * S::kStageBytes + TB);
-    if (!wave_active) return;
+    const int kt = kt_of(i);
+    if (i == i_tail) {
+      if (kt == kt_tail) {
+        char* vt = hsm + (i % NS) * S::kStageBytes + TB;
+        const int r0 = kend - kt * kKT;
+        for (int idx = htid; idx < (kKT - r0) * RC; idx += kThreads)
+          *reinterpret_cast<uint4*>(vt + (r0 + idx / RC) * RB + (idx % RC) * 16) = make_uint4(0u, 0u, 0u, 0u);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
+    if (kt >= ntiles || !wave_active) return;
+    const int sbase = smem_base + (i % NS) * S::kStageBytes;
     f32x16_t st[kNB];
     scores(sbase, st);
     finish(mask_tag, kt, st, sbase + TB);
   };
-  for (int kt = kt0; kt < nfull; ++kt) tile(std::false_type{}, kt);
-  for (int kt = max(kt0, nfull); kt < ntiles; ++kt) tile(std::true_type{}, kt);
+  const int i_full = min(nsteps, max(0, (nfull - kt0 - kh + KH - 1) / KH));  // this half's unmasked steps
+  int i = 0;
+  for (; i < i_full; ++i) step(std::false_type{}, i);
+  for (; i < nsteps; ++i) step(std::true_type{}, i);
 
   // no direct-to-LDS load may still be writing when the workgroup's LDS is released
   wait_vmcnt_le<0>();
   const int any_bad = __syncthreads_or(local_bad);
+  if constexpr (KH == 2) {
+    // the second half hands its state of each row (m, l and O^T, lane by lane)
+    // to the first through the LDS the rings no longer use
+    constexpr int kX = 2 + S::kND * 16;  // floats per lane
+    static_assert(kWaves * kX * 64 * 4 <= KH * NS * S::kStageBytes, "the states fit the rings' LDS");
+    float* x = reinterpret_cast<float*>(smem) + wave * kX * 64 + lane;
+    if (kh == 1) {
+      x[0] = m_run;
+      x[64] = l_run;
+#pragma unroll
+      for (int nd = 0; nd < S::kND; ++nd)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[(2 + nd * 16 + v) * 64] = oacc[nd][v];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = x[0];
+    const float mn = fmaxf(m_run, m1);
+    const float f0 = fast_exp2(m_run - mn), f1 = fast_exp2(m1 - mn);
+    l_run = l_run * f0 + x[64] * f1;
+#pragma unroll
+    for (int nd = 0; nd < S::kND; ++nd)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[nd][v] = oacc[nd][v] * f0 + x[(2 + nd * 16 + v) * 64] * f1;
+    m_run = mn;
+  }
   const float l_tot = l_run + shfl_xor_f32(l_run, 32);
   if (!row_ok) return;
   if (partial) {
@@ -623,21 +672,33 @@ __global__ __launch_bounds__(64) void prefill_split_merge_kernel(const PrefillAr
   for (int e = 0; e < PER; ++e) orow[lane + e * kWave] = (__bf16)(o[e] * inv);
 }
 
-template <int MODE>
-static hipError_t launch_chunk_modes(const PrefillArgs& a, int64_t grid, hipStream_t stream) {
+// Grids of at most this many workgroups (one per compute unit) take two key
+// halves per workgroup.
+#ifndef PKV_PREFILL_KEY_HALVES_GRID
+#define PKV_PREFILL_KEY_HALVES_GRID 256
+#endif
+
+template <int MODE, int KH>
+static hipError_t launch_chunk_halves(const PrefillArgs& a, int64_t grid, hipStream_t stream) {
   switch (a.head_dim) {
     case 64:
-      hipLaunchKernelGGL((prefill_mfma_kernel<64, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
-                         a.block_tables);
+      hipLaunchKernelGGL((prefill_mfma_kernel<64, MODE, KH>), dim3((unsigned)grid), dim3(kThreads * KH), 0, stream,
+                         a, a.block_tables);
       break;
     case 128:
-      hipLaunchKernelGGL((prefill_mfma_kernel<128, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
-                         a.block_tables);
+      hipLaunchKernelGGL((prefill_mfma_kernel<128, MODE, KH>), dim3((unsigned)grid), dim3(kThreads * KH), 0, stream,
+                         a, a.block_tables);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_chunk_modes(const PrefillArgs& a, int64_t grid, hipStream_t stream) {
+  if (grid <= PKV_PREFILL_KEY_HALVES_GRID) return launch_chunk_halves<MODE, 2>(a, grid, stream);
+  return launch_chunk_halves<MODE, 1>(a, grid, stream);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
