@@ -49,10 +49,10 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 # are used.  Keyed by (workload, --kv-dtype).  Valid only for the decode kernel
 # sources it was measured on: reported as null once their hash differs.
 TRAFFIC = {
-    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 509995827, "write_bytes": 3420979,
-                                        "sources_sha256": "76bc20fc7a0f434617548ed1818ae6ba383c0110e3effc63c36f3632a8785a11"},
-    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 273485005, "write_bytes": 3424666,
-                                      "sources_sha256": "76bc20fc7a0f434617548ed1818ae6ba383c0110e3effc63c36f3632a8785a11"},
+    ("llama3-8b-decode-bf16", "model"): {"read_bytes": 510129357, "write_bytes": 3504538,
+                                        "sources_sha256": "b0d266f68e368d214e06707c9f473097ae176871e5d0d1c7abf463467c8df583"},
+    ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 273598669, "write_bytes": 3508634,
+                                      "sources_sha256": "b0d266f68e368d214e06707c9f473097ae176871e5d0d1c7abf463467c8df583"},
 }
 CSRC = os.path.join(ROOT, "paged_kv_cache_295_amd", "csrc")
 DECODE_SOURCES = ("decode.hip", "pkv_device.hpp", "pkv_internal.hpp")

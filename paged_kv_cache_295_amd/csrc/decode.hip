@@ -1114,9 +1114,17 @@ hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int64_t r
 //
 // Sequences with a context outside [0, 16 * max_blocks] contribute no cost;
 // the merge kernel writes NaN for them (and 0 for an empty context).
+//
+// The charge is 4 block units.  Measured on one box, cold caches, two
+// rounds each (us per call; charge 2 / 3 / 4 / 5 / 6 / 8): Llama-3-8B batch
+// 89.5 / 90.4 / 89.6 / 90.0 / 90.3 / 91.8; its fp8 cache 56.5 / 56.2 / 55.8 /
+// 55.5 / 55.7 / 56.0; the shared-prefix call 95.9 / 94.3 / 93.2 / 93.6 / 93.2
+// / 93.7; the verify pass (64 x 5 rows) 105.0 / 102.7 / 101.4 / 101.6 / - /
+// 102.7; the mixed step's decode 137.3 / 137.6 / 137.3 / 137.7 / 137.8 /
+// 138.4; the long-context batch is the same at 4, 6 and 8 (457-458).
 
 #ifndef PKV_SEGMENT_COST
-#define PKV_SEGMENT_COST 8
+#define PKV_SEGMENT_COST 4
 #endif
 constexpr int kSegCost = PKV_SEGMENT_COST;
 
