@@ -412,6 +412,32 @@ def test_spec_verify_balanced_edges(case):
         assert (got[c, n:] == SENTINEL).all(), f"sequence {c}: rows past its count must not be written"
 
 
+@pytest.mark.parametrize("rows", [1, 5])
+def test_spec_verify_balanced_bad_block_gives_nan(rows):
+    """The balanced verify split with a block-table entry out of the pool: every valid row of that sequence
+    (block 0 is in every row's keys) is NaN, the others are unaffected; rows_max = 1 runs the split with a
+    single row per sequence."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    pairs = [(int(rng.integers(1, 900)), int(rng.integers(1, rows + 1))) for _ in range(16)]
+    w = chunk_workload("bf16", 32, 8, 128, pairs, seed=33, cmax=rows)
+    good_tables = w.chunk_tables.copy()
+    w.chunk_tables[3, 0] = w.num_blocks + 7
+    dw = DeviceWorkload(w)
+    rk, rv = run_write(dw)
+    out, need = run_verify(dw)
+    assert need == 1024 * 2 * (16 if 4 * rows <= 16 else 32) * 130 * 4, "the balanced split's workspace"
+    ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, good_tables, w.chunk_context_lens, w.scale,
+                               w.dtype)
+    got = values(out)
+    for c in range(w.num_chunks):
+        n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+        if c == 3:
+            assert np.isnan(got[c, :n]).all(), "the bad sequence's rows"
+        else:
+            check_attn(got[c, :n], ref[c, :n], w.dtype, f"sequence {c}")
+        assert (got[c, n:] == SENTINEL).all(), f"sequence {c}: rows past its count must not be written"
+
+
 def test_spec_verify_split_bad_sequence_gives_nan():
     """A sequence that breaks the contract (more rows than rows_max) gets NaN rows;
     the others are unaffected, with the keys split into pieces."""
