@@ -170,10 +170,11 @@ constexpr int balanced_waves_max(int gb) {
 // over kVerifyWaves waves, each leaving at most two partial slots of 16 or 32
 // columns.  Fewer streams keep the matrix-core chunk kernel with its key
 // split: their keys are cut into so many pieces over the 1024 waves that the
-// partials of 20 columns per piece cost more than the split saves (5 rows x
-// 32q / 8kv heads, contexts U{128..4096}, cold caches: 8 sequences 29.5 us
-// against 26.1 on the chunk kernel; 16 sequences 37.5 against 52.1; 32: 55.9
-// against 73.0; 64: 99.8 against 107.1; 128: 200.3 against 203.2).
+// partials of 20 columns per piece cost as much as the split saves (5 rows x
+// 32q / 8kv heads, contexts U{128..4096}, cold caches: 8 sequences 26.1 us
+// against 26.0 on the chunk kernel, the same at 256 and 512 waves; 16
+// sequences 37.5 against 52.1; 32: 55.9 against 73.0; 64: 99.8 against 107.1;
+// 128: 200.3 against 203.2).
 constexpr int kVerifyWaves = 1024;
 constexpr int64_t kVerifyMinStreams = 128;
 constexpr bool verify_balanced(int gb, int dtype, int head_dim, int rows) {
