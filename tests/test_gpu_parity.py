@@ -438,6 +438,38 @@ def test_spec_verify_balanced_bad_block_gives_nan(rows):
         assert (got[c, n:] == SENTINEL).all(), f"sequence {c}: rows past its count must not be written"
 
 
+def test_spec_verify_random_shapes():
+    """Seeded random verify batches: 4 or 8 query heads per kv head, 1, 2 or 8 kv heads, 1..8 rows,
+    sequences with no rows, empty and ragged accepted contexts; most reach the balanced split's threshold,
+    the rest take the chunk kernel (with or without its key split)."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    for case in range(16):
+        g = int(rng.choice([4, 8]))
+        hkv = int(rng.choice([1, 2, 8]))
+        rows = int(rng.integers(1, 32 // g + 1)) if rng.random() < 0.8 else int(rng.integers(1, 10))
+        nseq = int(rng.integers(1, 48))
+        if nseq * hkv < 128 and rng.random() < 0.7:
+            nseq = -(-128 // hkv)
+        pairs = []
+        for _ in range(nseq):
+            ctx = int(rng.choice([0, 1, 15, 16, 17, int(rng.integers(1, 2500))]))
+            n = int(rng.integers(0, rows + 1)) if rng.random() < 0.2 else int(rng.integers(1, rows + 1))
+            pairs.append((ctx, n))
+        w = chunk_workload("bf16", g * hkv, hkv, 128, pairs, seed=int(rng.integers(1, 1 << 30)), cmax=rows)
+        dw = DeviceWorkload(w)
+        rk, rv = run_write(dw)
+        out, need = run_verify(dw)
+        say(f"random verify case {case}: G={g} Hkv={hkv} rows={rows} sequences={nseq} workspace={need}")
+        ref = oracle.prefill_chunk(w.q_chunk, w.chunk_start, rk, rv, w.chunk_tables, w.chunk_context_lens,
+                                   w.scale, w.dtype)
+        got = values(out)
+        for c in range(w.num_chunks):
+            n = int(w.chunk_context_lens[c] - w.chunk_start[c])
+            if n:
+                check_attn(got[c, :n], ref[c, :n], w.dtype, f"random verify case {case}, sequence {c}")
+            assert (got[c, n:] == SENTINEL).all(), f"case {case}, sequence {c}: rows past its count written"
+
+
 def test_spec_verify_split_bad_sequence_gives_nan():
     """A sequence that breaks the contract (more rows than rows_max) gets NaN rows;
     the others are unaffected, with the keys split into pieces."""
