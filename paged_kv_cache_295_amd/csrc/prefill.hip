@@ -125,13 +125,19 @@ __host__ __device__ __forceinline__ int tile_rows(int chunk_len_max, int G) {
 }
 
 
-// LDS reads in one asm block each, completed before the block ends; read i
-// is at base[i] + O.
-template <int O, int N>
+// LDS reads, read i at base[i] + O.  ASM: in one asm block, completed before
+// the block ends.  Otherwise plain loads that the compiler schedules and
+// waits for one at a time (it must not see the direct-to-LDS loads as stores
+// it has to wait for: those are then issued from asm, see load_lds_x4).
+template <bool ASM, int O, int N>
 __device__ __forceinline__ void lds_read_b128(const int (&base)[N], u32x4_t (&r)[N]) {
   static_assert(N == 4 || N == 8, "4 or 8 reads");
   static_assert(O >= 0 && O < 65536, "ds offset is 16 bits");
-  if constexpr (N == 4) {
+  if constexpr (!ASM) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      r[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((uintptr_t)(uint32_t)(base[i] + O));
+  } else if constexpr (N == 4) {
     asm volatile(
         "ds_read_b128 %0, %4 offset:%8\n\tds_read_b128 %1, %5 offset:%8\n\t"
         "ds_read_b128 %2, %6 offset:%8\n\tds_read_b128 %3, %7 offset:%8\n\t"
@@ -151,11 +157,18 @@ __device__ __forceinline__ void lds_read_b128(const int (&base)[N], u32x4_t (&r)
   }
 }
 
-template <int O, int N>
+template <bool ASM, int O, int N>
 __device__ __forceinline__ void lds_read_tr16(const int (&base)[N], u32x2_t (&r)[N]) {
   static_assert(N == 4 || N == 8, "4 or 8 reads");
   static_assert(O >= 0 && O < 65536, "ds offset is 16 bits");
-  if constexpr (N == 4) {
+  if constexpr (!ASM) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      r[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+                                                 (uintptr_t)(uint32_t)(base[i] + O))));
+  } else if constexpr (N == 4) {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %4 offset:%8\n\tds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
         "ds_read_b64_tr_b16 %2, %6 offset:%8\n\tds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
@@ -180,6 +193,34 @@ __device__ __forceinline__ void wait_vmcnt_le() {
   static_assert(N >= 0 && N < 64, "vmcnt is six bits");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
 }
+
+// The ring's step boundary when the LDS reads are plain loads: this wave's
+// direct-to-LDS loads of the step are done (at most N remain) and so are its
+// LDS reads of the previous step, then the workgroup barrier; the asm
+// statements also keep the compiler from moving LDS reads across it.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One direct-to-LDS load of 16 bytes per lane: global address base + voff,
+// LDS address lds + 16 lane, from asm so that the compiler's wait insertion
+// does not put a wait for it before every LDS read (the ring's own waits
+// order the two).
+// M0 is clobbered: the kernels that use this set it nowhere else.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
+__device__ __forceinline__ void load_lds_x4(const char* base, int voff, int lds) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds) : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "m0");
+}
+#pragma clang diagnostic pop
 
 // MODE kChunk: chunked prefill (rows = chunk rows x G heads of one kv head,
 // keys 0 .. row position, causal).  MODE kPrefix: the shared prefix of a
@@ -207,6 +248,14 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   constexpr int RB = S::kRowBytes;
   constexpr int TB = S::kTileBytes;
   static_assert(KH == 1 || KH == 2, "one or two key halves");
+  // How the LDS reads are waited for.  Two key halves (one eight-wave
+  // workgroup per compute unit): plain loads, the compiler overlapping each
+  // read with the products of the reads before it (the mixed-step chunks
+  // 44 -> 42 us).  Four-wave workgroups, two per compute unit: each group of
+  // reads waited for at once in asm, the other workgroup's waves filling the
+  // wait (plain loads there: the large prefill 553 -> 560 us, the 8-sequence
+  // verify 26.7 -> 28.4 us).
+  constexpr bool ASMR = KH == 1;
   __shared__ __attribute__((aligned(1024))) char smem[KH * NS * S::kStageBytes];
 
   const int tid = threadIdx.x;
@@ -372,6 +421,20 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     const int64_t boff = (int64_t)p * blk_stride + (int64_t)g * tile_bytes;
     const char* kb = kc + boff;
     const char* vb = vc + boff;
+    if constexpr (!ASMR) {
+      const int kl = __builtin_amdgcn_readfirstlane((int)(uintptr_t)(__attribute__((address_space(3))) char*)kdst);
+#pragma unroll
+      for (int i = 0; i < S::kLoadsPerWave; ++i) {
+        if (stream_kv) {
+          load_lds_x4<true>(kb, goff[i], kl + i * 1024);
+          load_lds_x4<true>(vb, goffv[i], kl + TB + i * 1024);
+        } else {
+          load_lds_x4<false>(kb, goff[i], kl + i * 1024);
+          load_lds_x4<false>(vb, goffv[i], kl + TB + i * 1024);
+        }
+      }
+      return;
+    }
     constexpr int kNT = 2;  // cache-policy bit of the non-temporal hint
     if (stream_kv) {
 #pragma unroll
@@ -436,12 +499,16 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[nb][v] = 0.0f;
       u32x4_t kv[S::kKSteps];
-      if (nb == 0) lds_read_b128<0>(kb, kv);
-      else lds_read_b128<32 * RB>(kb, kv);
+      if (nb == 0) lds_read_b128<ASMR, 0>(kb, kv);
+      else lds_read_b128<ASMR, 32 * RB>(kb, kv);
 #pragma unroll
       for (int kk = 0; kk < S::kKSteps; ++kk)
         st[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[kk]), qop[kk], st[nb], 0, 0,
                                                          0);
+    }
+    if constexpr (!ASMR) {  // every K read of the tile first, then the products as the reads arrive
+      __builtin_amdgcn_sched_group_barrier(0x100, kNB * S::kKSteps, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kNB * S::kKSteps, 0);
     }
   };
 
@@ -509,10 +576,10 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
 #pragma unroll
         for (int i = 0; i < NR; ++i) vb[i] = vbase + voff[i];
         u32x2_t vv[NR];
-        if (nb == 0 && s == 0) lds_read_tr16<0>(vb, vv);
-        else if (nb == 0) lds_read_tr16<16 * RB>(vb, vv);
-        else if (s == 0) lds_read_tr16<32 * RB>(vb, vv);
-        else lds_read_tr16<48 * RB>(vb, vv);
+        if (nb == 0 && s == 0) lds_read_tr16<ASMR, 0>(vb, vv);
+        else if (nb == 0) lds_read_tr16<ASMR, 16 * RB>(vb, vv);
+        else if (s == 0) lds_read_tr16<ASMR, 32 * RB>(vb, vv);
+        else lds_read_tr16<ASMR, 48 * RB>(vb, vv);
 #pragma unroll
         for (int nd = 0; nd < S::kND; ++nd)
           oacc[nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -548,11 +615,20 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   auto step = [&](auto mask_tag, int i) {
     // this wave's loads of step i are done once at most NS-2 steps' loads remain;
     // the barrier then makes every wave's part visible and frees the stage of i-1
-    wait_vmcnt_le<(NS - 2) * S::kDW>();
-    __builtin_amdgcn_s_barrier();
-    {
+    if constexpr (ASMR) {
+      wait_vmcnt_le<(NS - 2) * S::kDW>();
+      __builtin_amdgcn_s_barrier();
       const int p = pnext;
       pnext = table_entry(kt_of(i + NS));
+      issue((i + NS - 1) % NS, p);
+    } else {
+      // the table entry of a later step is loaded and waited for before the
+      // barrier: a scalar load in flight would make the compiler wait for
+      // every LDS read at once (the two share a counter)
+      const int p = pnext;
+      pnext = table_entry(kt_of(i + NS));
+      asm volatile("" ::"s"(pnext));
+      ring_barrier<(NS - 2) * S::kDW>();
       issue((i + NS - 1) % NS, p);
     }
     const int kt = kt_of(i);
