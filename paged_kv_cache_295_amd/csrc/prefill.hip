@@ -647,16 +647,17 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
     const int sbase = smem_base + (i % NS) * S::kStageBytes;
     f32x16_t st[kNB];
     scores(sbase, st);
-    // Four-wave workgroups share a compute unit with a second workgroup: the
-    // wave past its score products (softmax, value products) takes issue
-    // priority over one starting its scores, so the two workgroups drift into
-    // alternating phases (the large prefill 551 / 544 -> 533 / 536 us cold on
-    // one box; priority for the scores instead: 542 us, for the value
-    // products alone: 565 us; with the key halves, whose groups share
-    // barriers, the mixed-step chunks went 43 -> 44 us, so they keep one level).
-    if constexpr (KH == 1) __builtin_amdgcn_s_setprio(1);
+    // Two waves share each SIMD (two four-wave workgroups, or the two key
+    // halves): the wave past its score products (softmax, value products)
+    // takes issue priority over one starting its scores, so the two drift
+    // into alternating phases (the large prefill 551 / 544 -> 533 / 536 us
+    // cold on one box; priority for the scores instead: 542 us, for the value
+    // products alone: 565 us; the key halves' mixed-step chunks 42.4 -> 40.6 us
+    // with their reads waited for one at a time, 43 -> 44 us with the reads
+    // of a group waited for at once).
+    __builtin_amdgcn_s_setprio(1);
     finish(mask_tag, kt, st, sbase + TB);
-    if constexpr (KH == 1) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   const int i_full = min(nsteps, max(0, (nfull - kt0 - kh + KH - 1) / KH));  // this half's unmasked steps
   int i = 0;
