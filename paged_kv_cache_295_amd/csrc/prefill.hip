@@ -368,16 +368,23 @@ void prefill_mfma_kernel(const PrefillArgs a, const int32_t* __restrict__ tables
   // (exact in bf16) and of the scale.
   const float sl2 = fabsf(a.scale_log2);
   const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  // Every lane loads its query chunks together, rows without a query from a
+  // row that exists (the chunk's first row of the group's first head), and
+  // zeroes them after: loads under the row test would each be waited for
+  // before the next is issued.
+  const __bf16* qsrc = row_ok ? qrow
+                              : reinterpret_cast<const __bf16*>(a.q) +
+                                    (PREFIX ? (int64_t)g * G * D
+                                            : ((int64_t)c * a.chunk_len_max * a.num_q_heads + g * G) * D);
+  Chunk qch[S::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < S::kKSteps; ++kk) qch[kk] = load_chunk(qsrc + kk * 16 + 8 * half);
+  const uint32_t qkeep = row_ok ? 0xffffffffu : 0u;
   bf16x8_t qop[S::kKSteps];
 #pragma unroll
-  for (int kk = 0; kk < S::kKSteps; ++kk) {
-    if (row_ok) {
-      const Chunk ch = load_chunk(qrow + kk * 16 + 8 * half);
-      qop[kk] = as_bf16x8(ch.w[0] ^ qsign, ch.w[1] ^ qsign, ch.w[2] ^ qsign, ch.w[3] ^ qsign);
-    } else {
-      qop[kk] = as_bf16x8(0u, 0u, 0u, 0u);
-    }
-  }
+  for (int kk = 0; kk < S::kKSteps; ++kk)
+    qop[kk] = as_bf16x8((qch[kk].w[0] ^ qsign) & qkeep, (qch[kk].w[1] ^ qsign) & qkeep,
+                        (qch[kk].w[2] ^ qsign) & qkeep, (qch[kk].w[3] ^ qsign) & qkeep);
 
   // ---- load side: this wave's block (key rows 16 wave .. 16 wave + 15) of each tile
   const int32_t* __restrict__ table = tables + (int64_t)c * a.max_blocks_per_seq;
